@@ -1,0 +1,68 @@
+"""Oracle: forward and backward of the QLoRA linear layer, in float64.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Definitions ([Explainer] "The QLoRA layer, end to end", the one-layer code
+listing; [Explainer] "LoRA: freeze the base, train a patch" for s = alpha/r;
+[Review] "The Gradient Flow Trick" states the same gradients with s = 1):
+
+    forward:   Y  = X W + s (X L1) L2
+    backward:  dX = dY W^T + s (dY L2^T) L1^T
+               dL1 = s X^T (dY L2^T)
+               dL2 = s (X L1)^T dY
+    and no gradient for the frozen W.
+
+Here W is the page's [in][out] matrix.  The stored weight is the [out][in]
+row-major matrix Wq (the layout of a torch Linear weight), so the page's W is
+Wq^T and the dequantized weight enters as X Wq^T.  L1 = A [in][r], L2 = B [r][out].
+
+All inputs are bf16 bit patterns; every product runs in float64 on the exact
+bf16 values with no intermediate rounding.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _f64(u16) -> np.ndarray:
+    return (np.asarray(u16, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def forward(X, Wq, A, B, s: float):
+    """Returns (Y [M][out], T = X A [M][r]) in float64."""
+    x, w, a, b = _f64(X), _f64(Wq), _f64(A), _f64(B)
+    t = x @ a
+    y = x @ w.T + s * (t @ b)
+    return y, t
+
+
+def backward(dY, X, Wq, A, B, s: float):
+    """Returns (dX [M][in], dA [in][r], dB [r][out]) in float64."""
+    dy, x, w, a, b = _f64(dY), _f64(X), _f64(Wq), _f64(A), _f64(B)
+    g = dy @ b.T                    # dY L2^T
+    dx = dy @ w + s * (g @ a.T)     # passes through the frozen weight
+    da = s * (x.T @ g)
+    db = s * ((x @ a).T @ dy)
+    return dx, da, db
+
+
+def forward_rows(X, Wq, A, B, s: float, rows):
+    """Y for selected token rows only (sampled checks at full size)."""
+    rows = np.asarray(rows)
+    return forward(np.asarray(X)[rows], Wq, A, B, s)[0]
+
+
+def backward_dx_rows(dY, Wq, A, B, s: float, rows):
+    """dX for selected token rows only (sampled checks at full size)."""
+    rows = np.asarray(rows)
+    dy, w, a, b = _f64(np.asarray(dY)[rows]), _f64(Wq), _f64(A), _f64(B)
+    return dy @ w + s * ((dy @ b.T) @ a.T)
+
+
+def flops_fwd(M, d_in, d_out, r) -> int:
+    return 2 * M * d_in * d_out + 2 * M * r * (d_in + d_out)
+
+
+def flops_fwd_bwd(M, d_in, d_out, r) -> int:
+    """fwd (2 M in out + 2 M r (in+out)) + bwd without dW (2 M in out + 4 M r (in+out))."""
+    return 4 * M * d_in * d_out + 6 * M * r * (d_in + d_out)

@@ -1,0 +1,333 @@
+"""Oracle: NF4 blockwise quantization with double quantization, and its inverse.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).  Plain NumPy, written
+for reading, not for speed.  bf16 values travel as uint16 bit patterns.
+
+What is fixed by the pages, and where:
+  * NF4 levels: 16 values built from standard-normal quantiles, the two tails
+    pulled in by an offset of 0.9677083, 8 positive levels, 7 negative levels and
+    an exact zero, the whole set divided by its largest magnitude so that the
+    ends are exactly -1 and +1 ([Explainer] "NormalFloat: 4 bits for a bell
+    curve", the code-point listing and the two paragraphs around it).
+  * Absmax scaling: the scale constant is c = (largest code) / absmax, a value
+    is normalized by multiplying it with c ([Explainer] "Quantize in blocks, not
+    all at once", the Int8 absmax formula and its dequant).  For NF4 the largest
+    code is 1, so c = 1/absmax.
+  * Blocks of 64 contiguous weights of the flattened tensor, one constant each
+    ([Explainer] "Quantize in blocks, not all at once"; [Addaly] "NF4, and why
+    not plain int4").
+  * Nearest level ([Review] "What QLoRA Actually Does", item 1).
+  * Double quantization: the block constants, after subtracting their mean, are
+    stored as 8-bit floats in groups of 256 with one 32-bit scale per group
+    ([Explainer] "Double quantization"; [Glossary] calls the 8-bit type FP8).
+  * doubleDequant: first rebuild the block scales from c2 (8-bit) and c1
+    (fp32), then turn the 4-bit codes into bf16 with those scales ([Explainer]
+    "The QLoRA layer, end to end").
+
+Readings where the pages leave a step open (each is listed in the design notes):
+  R1  levels computed in float64 by the printed procedure, rounded once to fp32;
+  R2  x = fl32(w * fl32(1/absmax)) with a correctly rounded reciprocal;
+  R3  nearest fp32 level in exact arithmetic, ties to the lower index;
+  R4  a block whose absmax is below the smallest normal fp32 (2^-126) is a zero
+      block: stored absmax 0, every code 7 (the exact zero);
+  R5  W is the [out][in] row-major weight; blocks run along the flattened array;
+  R6  element 2i goes to bits 7..4 of byte i, element 2i+1 to bits 3..0; a final
+      odd element is padded with code 7;
+  R7  the 8-bit float is OCP FP8 E4M3 (max 448), round to nearest even, the
+      group's largest centered magnitude mapped to 448;
+  R8  one mean per tensor, mu = fl32(S / nblk) with S the correctly rounded
+      float64 value of the exact sum of the stored absmax values;
+  R9  c1 = fl32(m / 448); a group whose c1 is below 2^-126 stores c1 = 0 and
+      all c2 = 0; otherwise c2 = E4M3(fl32(fl32(a - mu) * fl32(1/c1)));
+  R10 s' = fl32(fl32(dec(c2) * c1) + mu), two roundings, no fused multiply-add;
+  R11 the codes use the true absmax; dequant uses s';
+  R12 dequantized weight = bf16_RNE(fl32(level[code] * s')).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+OFFSET = 0.9677083      # [Explainer] "NormalFloat", code-point listing
+BLOCK = 64              # [Explainer] "Quantize in blocks"; [Addaly] "NF4, and why not plain int4"
+SUPER = 256             # [Explainer] "Double quantization"; [Addaly] same section
+FP8_MAX = 448.0         # largest finite OCP E4M3 value (reading R7)
+FP32_MIN_NORMAL = 2.0 ** -126
+ZERO_CODE = 7           # index of the exact zero among the sorted levels
+
+_CHUNK = 1 << 20
+
+
+# ----------------------------------------------------------------------------------------------
+# bf16 <-> fp32 (bit level)
+# ----------------------------------------------------------------------------------------------
+def bf16_to_f32(u16: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> fp32 values (exact)."""
+    return (np.asarray(u16, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def f32_to_bf16(x: np.ndarray) -> np.ndarray:
+    """fp32 values -> bf16 bit patterns, round to nearest, ties to even.  Finite inputs only."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if np.isnan(x).any():
+        raise ValueError("NaN has no defined rounding here")
+    b = x.view(np.uint32).astype(np.uint64)
+    lsb = (b >> 16) & 1
+    return ((b + 0x7FFF + lsb) >> 16).astype(np.uint16)
+
+
+# ----------------------------------------------------------------------------------------------
+# NF4 codebook
+# ----------------------------------------------------------------------------------------------
+def _default_ppf(p):
+    from scipy.special import ndtri
+
+    return ndtri(p)
+
+
+def nf4_levels_f64(ppf=None) -> np.ndarray:
+    """The 16 NF4 levels in float64, by the procedure of [Explainer] "NormalFloat".
+
+    8 positive quantiles at probabilities evenly spaced from OFFSET down to 1/2
+    (1/2 itself excluded), 7 negative ones mirrored the same way with 8 points,
+    plus an exact zero; sorted and divided by the largest magnitude.
+    """
+    ppf = ppf or _default_ppf
+    pos = np.asarray(ppf(np.linspace(OFFSET, 0.5, 9)[:-1]), dtype=np.float64)
+    neg = -np.asarray(ppf(np.linspace(OFFSET, 0.5, 8)[:-1]), dtype=np.float64)
+    v = np.sort(np.concatenate([neg, [0.0], pos]))
+    return v / np.max(np.abs(v))
+
+
+def nf4_levels(ppf=None) -> np.ndarray:
+    """The NF4 levels rounded once to fp32 (reading R1)."""
+    return nf4_levels_f64(ppf).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------------------------
+# First-level quantization: blockwise absmax + nearest NF4 level
+# ----------------------------------------------------------------------------------------------
+def num_blocks(numel: int) -> int:
+    return -(-numel // BLOCK)
+
+
+def num_super(nblk: int) -> int:
+    return -(-nblk // SUPER)
+
+
+def _blocks_f32(w_bits: np.ndarray) -> np.ndarray:
+    """Flattened weight as fp32 values, zero padded to whole blocks, shape [nblk, 64]."""
+    flat = bf16_to_f32(np.ravel(w_bits))
+    nblk = num_blocks(flat.size)
+    out = np.zeros(nblk * BLOCK, dtype=np.float32)
+    out[: flat.size] = flat
+    return out.reshape(nblk, BLOCK)
+
+
+def blockwise_absmax(w_bits: np.ndarray) -> np.ndarray:
+    """Largest magnitude of each 64-block (padding is zero so it never wins); reading R4 applied."""
+    a = np.abs(_blocks_f32(w_bits)).max(axis=1)
+    a[a < np.float32(FP32_MIN_NORMAL)] = 0.0
+    return a.astype(np.float32)
+
+
+def nearest_level(x: np.ndarray, levels: np.ndarray | None = None) -> np.ndarray:
+    """Index of the nearest level to each fp32 x, ties to the lower index (reading R3).
+
+    Brute force over the 16 levels in float64.  x and the levels are fp32, so
+    x - level is exact in float64 whenever the two are within 29 binades of one
+    another, which covers every case where two distances could be equal or
+    close; argmin returns the first (lower) index on ties.
+    """
+    lv = (nf4_levels() if levels is None else levels).astype(np.float64)
+    x = np.ravel(np.asarray(x, dtype=np.float32))
+    out = np.empty(x.size, dtype=np.uint8)
+    for s in range(0, x.size, _CHUNK):
+        xs = x[s:s + _CHUNK].astype(np.float64)
+        out[s:s + _CHUNK] = np.argmin(np.abs(xs[:, None] - lv[None, :]), axis=1)
+    return out
+
+
+def normalize_blocks(blocks: np.ndarray, absmax: np.ndarray) -> np.ndarray:
+    """x = fl32(w * fl32(1/absmax)) per block (reading R2); zero blocks give x = 0."""
+    inv = np.zeros_like(absmax, dtype=np.float32)
+    nz = absmax > 0
+    inv[nz] = np.float32(1.0) / absmax[nz]
+    x = (blocks * inv[:, None]).astype(np.float32)
+    x[~nz] = 0.0
+    return x
+
+
+def nf4_codes(w_bits: np.ndarray, absmax: np.ndarray | None = None) -> np.ndarray:
+    """Unpacked 4-bit codes (one uint8 per element, padded to whole blocks)."""
+    blocks = _blocks_f32(w_bits)
+    if absmax is None:
+        absmax = blockwise_absmax(w_bits)
+    codes = np.empty(blocks.shape, dtype=np.uint8)
+    rows_per_chunk = max(1, _CHUNK // BLOCK)
+    for s in range(0, blocks.shape[0], rows_per_chunk):
+        x = normalize_blocks(blocks[s:s + rows_per_chunk], absmax[s:s + rows_per_chunk])
+        codes[s:s + rows_per_chunk] = nearest_level(x).reshape(x.shape)
+    codes[absmax == 0] = ZERO_CODE
+    return codes.reshape(-1)
+
+
+def codes_for_blocks(w_bits: np.ndarray, absmax: np.ndarray, block_ids: np.ndarray) -> np.ndarray:
+    """Unpacked codes [len(block_ids), 64] of selected blocks only (for sampled checks at full size)."""
+    flat = np.ravel(w_bits)
+    block_ids = np.asarray(block_ids, dtype=np.int64)
+    blocks = np.zeros((block_ids.size, BLOCK), dtype=np.float32)
+    for i, b in enumerate(block_ids):
+        seg = bf16_to_f32(flat[b * BLOCK:(b + 1) * BLOCK])
+        blocks[i, : seg.size] = seg
+    a = absmax[block_ids]
+    codes = nearest_level(normalize_blocks(blocks, a)).reshape(blocks.shape)
+    codes[a == 0] = ZERO_CODE
+    return codes
+
+
+def pack_nibbles(codes: np.ndarray, numel: int) -> np.ndarray:
+    """Two codes per byte, element 2i in the high nibble (reading R6); ceil(numel/2) bytes."""
+    c = np.full(2 * (-(-numel // 2)), ZERO_CODE, dtype=np.uint8)
+    c[:numel] = np.ravel(codes)[:numel]
+    return ((c[0::2] << 4) | c[1::2]).astype(np.uint8)
+
+
+def unpack_nibbles(packed: np.ndarray, numel: int) -> np.ndarray:
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(2 * p.size, dtype=np.uint8)
+    out[0::2] = p >> 4
+    out[1::2] = p & 0x0F
+    return out[:numel]
+
+
+# ----------------------------------------------------------------------------------------------
+# FP8 E4M3 (the 8-bit float of the second quantization; reading R7)
+# ----------------------------------------------------------------------------------------------
+def e4m3_encode(y: np.ndarray) -> np.ndarray:
+    """fp32 -> OCP E4M3 code, round to nearest even; magnitudes above 448 clamp to 448.
+
+    Normal codes: exponent field e in 1..15 (bias 7), 3 fraction bits; field 0
+    holds the subnormals m * 2^-9.  Code 0x7F (and 0xFF) is NaN and is never
+    produced.  The sign of a value that rounds to zero is kept.
+    """
+    y = np.asarray(y, dtype=np.float32)
+    a = np.abs(y.astype(np.float64)).ravel()
+    code = np.zeros(a.size, dtype=np.int64)
+    sub = a < 2.0 ** -6
+    code[sub] = np.rint(a[sub] * 2.0 ** 9).astype(np.int64)          # 0..8; 8 is the smallest normal
+    nor = ~sub
+    mant, ex = np.frexp(a[nor])                                        # a = mant * 2^ex, mant in [0.5, 1)
+    e = ex.astype(np.int64) - 1                                        # a = (2 mant) * 2^e
+    q = np.rint((2.0 * mant - 1.0) * 8.0).astype(np.int64)            # 3-bit fraction, 0..8
+    e = np.where(q == 8, e + 1, e)
+    q = np.where(q == 8, 0, q)
+    code[nor] = (e + 7) * 8 + q
+    code = np.minimum(code, 0x7E)
+    code |= np.signbit(y).ravel().astype(np.int64) << 7
+    return code.astype(np.uint8).reshape(y.shape)
+
+
+def e4m3_decode(c: np.ndarray) -> np.ndarray:
+    """OCP E4M3 code -> fp32 value (exact)."""
+    c = np.asarray(c, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e == 0, m * 2.0 ** -9, (8 + m) * np.exp2(e.astype(np.float64) - 10.0))
+    mag = np.where((c & 0x7F) == 0x7F, np.nan, mag)
+    return (sign * mag).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------------------------
+# Double quantization of the block constants
+# ----------------------------------------------------------------------------------------------
+def absmax_mean(absmax: np.ndarray) -> np.float32:
+    """mu = fl32(S / nblk), S = the correctly rounded float64 sum of all block constants (R8)."""
+    a = np.asarray(absmax, dtype=np.float32)
+    s = math.fsum(a.astype(np.float64).tolist())
+    return np.float32(s / a.size)
+
+
+def double_quantize(absmax: np.ndarray):
+    """Block constants -> (c2 uint8 [nblk], c1 fp32 [nsup], mu fp32); readings R7..R9."""
+    a = np.asarray(absmax, dtype=np.float32)
+    nblk = a.size
+    nsup = num_super(nblk)
+    mu = absmax_mean(a)
+    x = (a - mu).astype(np.float32)                                    # fl32(a - mu)
+    xp = np.zeros(nsup * SUPER, dtype=np.float32)
+    xp[:nblk] = x
+    m = np.abs(xp.reshape(nsup, SUPER)).max(axis=1)
+    c1 = (m / np.float32(FP8_MAX)).astype(np.float32)                 # fl32(m / 448)
+    c1[c1 < np.float32(FP32_MIN_NORMAL)] = 0.0
+    inv = np.zeros_like(c1)
+    nz = c1 > 0
+    inv[nz] = np.float32(1.0) / c1[nz]
+    sup = np.arange(nblk) // SUPER
+    y = (x * inv[sup]).astype(np.float32)                              # fl32(x * fl32(1/c1))
+    c2 = e4m3_encode(y)
+    c2[~nz[sup]] = 0
+    return c2, c1, mu
+
+
+def block_scales_dq(c2: np.ndarray, c1: np.ndarray, mu: np.float32) -> np.ndarray:
+    """Inner dequant of doubleDequant: s' = fl32(fl32(dec(c2) * c1) + mu) (reading R10)."""
+    sup = np.arange(np.asarray(c2).size) // SUPER
+    prod = (e4m3_decode(c2) * np.asarray(c1, dtype=np.float32)[sup]).astype(np.float32)
+    return (prod + np.float32(mu)).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------------------------
+# Whole-tensor quantize / dequantize
+# ----------------------------------------------------------------------------------------------
+def quantize(w_bits: np.ndarray, double_quant: bool = True) -> dict:
+    """Quantize a bf16 weight (any shape; flattened row-major) to NF4 with optional double quant."""
+    numel = int(np.asarray(w_bits).size)
+    absmax = blockwise_absmax(w_bits)
+    codes = nf4_codes(w_bits, absmax)
+    q = {"numel": numel, "codes": pack_nibbles(codes, numel), "absmax_true": absmax,
+         "double_quant": bool(double_quant)}
+    if double_quant:
+        c2, c1, mu = double_quantize(absmax)
+        q.update(c2=c2, c1=c1, mu=mu, scales=block_scales_dq(c2, c1, mu))
+    else:
+        q.update(scales=absmax.copy())
+    return q
+
+
+def dequantize_codes(codes_unpacked: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Outer dequant: bf16_RNE(fl32(level[code] * s')) per element (reading R12)."""
+    lv = nf4_levels()
+    c = np.asarray(codes_unpacked, dtype=np.uint8).ravel()
+    blk = np.arange(c.size) // BLOCK
+    out = np.empty(c.size, dtype=np.uint16)
+    for s in range(0, c.size, _CHUNK):
+        prod = (lv[c[s:s + _CHUNK]] * scales[blk[s:s + _CHUNK]]).astype(np.float32)
+        out[s:s + _CHUNK] = f32_to_bf16(prod)
+    return out
+
+
+def dequantize(q: dict, shape=None) -> np.ndarray:
+    """doubleDequant of a quantized tensor -> bf16 bit patterns (flattened, or reshaped)."""
+    numel = q["numel"]
+    out = dequantize_codes(unpack_nibbles(q["codes"], numel), q["scales"])
+    return out.reshape(shape) if shape is not None else out
+
+
+# ----------------------------------------------------------------------------------------------
+# Storage accounting ([Explainer] "Double quantization" and "The QLoRA layer, end to end")
+# ----------------------------------------------------------------------------------------------
+def storage_bytes(numel: int, double_quant: bool = True) -> dict:
+    """Bytes of each stored buffer: codes, block constants, second-level scales, mean."""
+    nblk = num_blocks(numel)
+    if double_quant:
+        return {"codes": -(-numel // 2), "absmax": nblk, "c1": 4 * num_super(nblk), "mu": 4}
+    return {"codes": -(-numel // 2), "absmax": 4 * nblk, "c1": 0, "mu": 0}
+
+
+def constant_bits_per_param(numel: int, double_quant: bool = True) -> float:
+    """Bits of quantization constants per weight (everything except the 4-bit codes)."""
+    b = storage_bytes(numel, double_quant)
+    return 8.0 * (b["absmax"] + b["c1"] + b["mu"]) / numel
