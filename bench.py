@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Benchmark of the QLoRA linear hot path on one MI355X.
+
+Headline workload: the 7B-shaped attention projection, W 4096x4096 (bf16,
+N(0, 0.02^2)) quantized to NF4 with double quantization, LoRA rank 64
+(alpha 16, s = 0.25), X of 2048 tokens (batch 4 x seq 512).  One step is the
+whole hot path on one batch: quantize + double-quantize the weight, forward
+(X A, fused dequant GEMM with the adapter term), backward (dY B^T, fused
+dequant dX GEMM, dA, dB).  `value` counts the forward+backward FLOPs
+4 M in out + 6 M r (in + out) (no dW; dequantization and quantization not
+counted) per step time, inputs already resident in HBM.  Four independent input
+sets are rotated so consecutive steps do not hit in the 256 MB Infinity Cache.
+
+Also reported:
+  roofline     -- the dominant kernel's algorithmic FLOPs per launch over its
+                  average duration (HIP events around every launch, in a
+                  separate pass of the same steps), against 2.5 PFLOP/s bf16;
+  gemv         -- the skinny-token forward at the 65B shapes (8192->22016 and
+                  22016->8192, M in {1,4,16}): packed-weight GB/s against 8 TB/s,
+                  rotating 6 weight copies (> 512 MB) per shape;
+  cpu_baseline -- the float64 NumPy oracle doing one full step of the headline
+                  workload on the host cores.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "QLoRA linear fwd+bwd TFLOP/s (large M) + dequant-GEMV weight GB/s (M≤16)"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBPS = 8000.0
+
+
+def flops_fwd_bwd(M, din, dout, r):
+    return 4 * M * din * dout + 6 * M * r * (din + dout)
+
+
+def weight_bytes(din, dout):
+    n = din * dout
+    nblk = -(-n // 64)
+    return 32 * nblk + nblk + 4 * (-(-nblk // 256)) + 4
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--sets", type=int, default=4, help="independent input sets rotated across steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gemv", action="store_true")
+    ap.add_argument("--gemv-iters", type=int, default=50)
+    ap.add_argument("--only", choices=["all", "headline", "gemv"], default="all",
+                    help="restrict the run (for profiling single kernels)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark measures one GPU only; the hot path is not run across "
+                                   "several GPUs (see the design notes for how it would shard)",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+
+    import bit_nf4_quantized_11_amd as Q
+    import workloads
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    M, din, dout, r, alpha = 2048, 4096, 4096, 64, 16.0
+    s = alpha / r
+    flops = flops_fwd_bwd(M, din, dout, r)
+    result = {"metric": METRIC, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+              "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+              "data": "synthetic (seeded Gaussian, LLaMA-7B layer shape)"}
+    result["config"] = {"workload": "QLoRA linear 4096->4096, 2048 tokens, NF4 block 64 + double quant 256, "
+                                    "LoRA r=64 alpha=16; step = quantize + forward + backward",
+                        "M": M, "in": din, "out": dout, "r": r, "alpha": alpha, "input_sets": args.sets,
+                        "flops_per_step": flops}
+
+    if args.only in ("all", "headline"):
+        sets = []
+        for i in range(args.sets):
+            seed = 2000 + 100 * i
+            sets.append(dict(
+                W=workloads.device_normal_bf16(seed + 0, (dout, din), 0.02),
+                A=workloads.device_normal_bf16(seed + 1, (din, r), 0.02),
+                B=workloads.device_normal_bf16(seed + 2, (r, dout), 0.02),
+                X=workloads.device_normal_bf16(seed + 3, (M, din), 1.0),
+                dY=workloads.device_normal_bf16(seed + 4, (M, dout), 1.0),
+                w=Q.nf4_alloc(dout, din, True, dev),
+                Y=torch.empty((M, dout), dtype=torch.bfloat16, device=dev),
+                T=torch.empty((M, r), dtype=torch.bfloat16, device=dev),
+                dX=torch.empty((M, din), dtype=torch.bfloat16, device=dev),
+                dA=torch.empty((din, r), dtype=torch.float32, device=dev),
+                dB=torch.empty((r, dout), dtype=torch.float32, device=dev)))
+        ws = torch.empty(max(Q.qlora_quantize_workspace(dout, din), Q.qlora_fwd_workspace(M, din, dout, r),
+                             Q.qlora_bwd_workspace(M, din, dout, r)), dtype=torch.uint8, device=dev)
+
+        def step(i):
+            d = sets[i % len(sets)]
+            Q.qlora_quantize_nf4(d["W"], True, out=d["w"], workspace=ws)
+            Q.qlora_linear_fwd(d["X"], d["w"], d["A"], d["B"], s, Y=d["Y"], T_save=d["T"], workspace=ws)
+            Q.qlora_linear_bwd(d["dY"], d["X"], d["T"], d["w"], d["A"], d["B"], s, dX=d["dX"], dA=d["dA"],
+                               dB=d["dB"], workspace=ws)
+
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        ev0.record()
+        for i in range(args.steps):
+            step(i)
+        ev1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = ev0.elapsed_time(ev1) / args.steps
+        result["ms_per_step"] = ms
+        result["value"] = flops / (ms * 1e-3) / 1e12
+        result["wall_s_timed"] = wall
+
+        # per-kernel durations: same steps again with HIP events around every launch
+        Q.qlora_profile_enable(True)
+        Q.qlora_profile_read(reset=True)
+        for i in range(args.steps):
+            step(i)
+        torch.cuda.synchronize()
+        prof = Q.qlora_profile_read(reset=True)
+        Q.qlora_profile_enable(False)
+        kern = {k: {"launches": n, "avg_us": 1e3 * t / n, "us_per_step": 1e3 * t / args.steps}
+                for k, (n, t) in prof.items()}
+        result["kernels"] = kern
+        # algorithmic FLOPs per launch of the two dequantizing GEMMs
+        algo = {"k_fwd_nf4_gemm": 2 * M * din * dout + 2 * M * r * dout,
+                "k_bwd_dx_nf4_gemm": 2 * M * dout * din + 2 * M * r * din}
+        dom = max((k for k in kern if k in algo), key=lambda k: kern[k]["us_per_step"])
+        ach = algo[dom] / (kern[dom]["avg_us"] * 1e-6) / 1e12
+        result["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
+                              "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS, "traffic": None,
+                              "flops_per_launch": algo[dom], "avg_us": kern[dom]["avg_us"]}
+        fb_us = sum(v["us_per_step"] for k, v in kern.items() if k not in ("k_nf4_quantize", "k_dq_mean",
+                                                                              "k_dq_encode", "k_fill_u32"))
+        result["fwd_bwd_kernel_tflops"] = flops / (fb_us * 1e-6) / 1e12
+        del sets, ws
+        torch.cuda.empty_cache()
+
+    if args.only in ("all", "gemv") and not args.no_gemv:
+        result["gemv"] = bench_gemv(Q, workloads, torch, dev, args.gemv_iters)
+
+    if args.only in ("all", "headline") and not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(M, din, dout, r, alpha, flops)
+
+    print(json.dumps(result))
+
+
+def bench_gemv(Q, workloads, torch, dev, iters):
+    """Skinny-token forward at the 65B shapes; weight GB/s on the packed weight."""
+    out = {"unit": "GB/s", "peak": PEAK_HBM_GBPS, "bound": "hbm", "copies": 6, "cases": {}}
+    r = 64
+    s = 16.0 / r
+    for din, dout in ((8192, 22016), (22016, 8192)):
+        copies = []
+        for c in range(6):
+            W = workloads.device_normal_bf16(4000 + 10 * c, (dout, din), 0.02)
+            copies.append(Q.qlora_quantize_nf4(W, True))
+            del W
+        A = workloads.device_normal_bf16(4001, (din, r), 0.02)
+        B = workloads.device_normal_bf16(4002, (r, dout), 0.02)
+        wb = weight_bytes(din, dout)
+        for M in (1, 4, 16):
+            X = workloads.device_normal_bf16(4003 + M, (M, din), 1.0)
+            Y = torch.empty((M, dout), dtype=torch.bfloat16, device=dev)
+            ws = torch.empty(Q.qlora_fwd_workspace(M, din, dout, r), dtype=torch.uint8, device=dev)
+            for i in range(10):
+                Q.qlora_linear_fwd(X, copies[i % 6], A, B, s, Y=Y, save_T=False, workspace=ws)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(iters):
+                Q.qlora_linear_fwd(X, copies[i % 6], A, B, s, Y=Y, save_T=False, workspace=ws)
+            e1.record()
+            torch.cuda.synchronize()
+            us = 1e3 * e0.elapsed_time(e1) / iters
+            Q.qlora_profile_enable(True)
+            Q.qlora_profile_read(reset=True)
+            for i in range(iters):
+                Q.qlora_linear_fwd(X, copies[i % 6], A, B, s, Y=Y, save_T=False, workspace=ws)
+            torch.cuda.synchronize()
+            prof = Q.qlora_profile_read(reset=True)
+            Q.qlora_profile_enable(False)
+            k = prof.get("k_fwd_nf4_gemv")
+            kus = 1e3 * k[1] / k[0] if k else None
+            out["cases"][f"{din}->{dout} M={M}"] = {
+                "us_per_forward": us, "weight_GBps": wb / (us * 1e-6) / 1e9,
+                "gemv_kernel_us": kus, "gemv_kernel_weight_GBps": (wb / (kus * 1e-6) / 1e9) if kus else None,
+                "kernels_us": {kk: 1e3 * t / n for kk, (n, t) in prof.items()}}
+        del copies
+        torch.cuda.empty_cache()
+    best = max(v["weight_GBps"] for v in out["cases"].values())
+    worst = min(v["weight_GBps"] for v in out["cases"].values())
+    out["weight_GBps_min"] = worst
+    out["weight_GBps_max"] = best
+    out["frac_min"] = worst / PEAK_HBM_GBPS
+    return out
+
+
+def cpu_baseline(M, din, dout, r, alpha, flops):
+    """The oracle as it stands: one full step (quantize + forward + backward) in float64 NumPy."""
+    import numpy as np
+
+    import workloads
+    from oracle import linear, nf4
+
+    lin = workloads.Linear("proj", M, din, dout, r, alpha)
+    inp = workloads.linear_inputs(2, lin)
+    reps, total = 0, 0.0
+    while reps < 5 and (reps == 0 or total < 10.0):   # about 10 s of CPU work
+        t0 = time.perf_counter()
+        q = nf4.quantize(inp.W, double_quant=True)
+        Wd = nf4.dequantize(q, (dout, din))
+        linear.forward(inp.X, Wd, inp.A, inp.B, lin.scale)
+        linear.backward(inp.dY, inp.X, Wd, inp.A, inp.B, lin.scale)
+        total += time.perf_counter() - t0
+        reps += 1
+    dt = total / reps
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max((i.get("num_threads", 0) for i in threadpool_info()), default=None)
+    except Exception:
+        pass
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads or len(os.sched_getaffinity(0)),
+            "kind": "oracle", "seconds_per_step": dt, "repeats": reps,
+            "sample": "full steps of the headline workload (quantize + dequantize + forward + backward), "
+                      "float64 NumPy, BLAS threads = cores, averaged over the repeats"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,80 @@
+"""ctypes declarations of the libqlora C ABI (include/qlora.h)."""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libqlora.so")
+
+STATUS = {
+    0: "QLORA_OK",
+    1: "QLORA_ERR_NULL",
+    2: "QLORA_ERR_SHAPE",
+    3: "QLORA_ERR_ALIGN",
+    4: "QLORA_ERR_UNSUPPORTED",
+    5: "QLORA_ERR_WORKSPACE",
+    6: "QLORA_ERR_HIP",
+}
+
+
+class qlora_nf4(C.Structure):
+    _fields_ = [
+        ("rows", C.c_int64),
+        ("cols", C.c_int64),
+        ("double_quant", C.c_int32),
+        ("reserved", C.c_int32),
+        ("codes", C.c_void_p),
+        ("absmax", C.c_void_p),
+        ("c1", C.c_void_p),
+        ("mu", C.c_void_p),
+    ]
+
+
+class qlora_kernel_time(C.Structure):
+    _fields_ = [("name", C.c_char * 48), ("launches", C.c_int64), ("total_ms", C.c_double)]
+
+
+# name -> (restype, argtypes); every name is declared in include/qlora.h
+SIGNATURES = {
+    "qlora_status_str": (C.c_char_p, [C.c_int]),
+    "qlora_version": (C.c_char_p, []),
+    "qlora_nf4_codebook": (C.c_int, [C.POINTER(C.c_float), C.POINTER(C.c_float)]),
+    "qlora_nf4_sizes": (C.c_int, [C.c_int64, C.c_int64, C.c_int32, C.POINTER(C.c_size_t), C.POINTER(C.c_size_t),
+                                  C.POINTER(C.c_size_t), C.POINTER(C.c_size_t)]),
+    "qlora_quantize_workspace": (C.c_size_t, [C.c_int64, C.c_int64, C.c_int32]),
+    "qlora_fwd_workspace": (C.c_size_t, [C.c_int64, C.c_int64, C.c_int64, C.c_int32]),
+    "qlora_bwd_workspace": (C.c_size_t, [C.c_int64, C.c_int64, C.c_int64, C.c_int32]),
+    "qlora_quantize_nf4": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.POINTER(qlora_nf4), C.c_void_p, C.c_size_t,
+                                     C.c_void_p]),
+    "qlora_dequant": (C.c_int, [C.POINTER(qlora_nf4), C.c_void_p, C.c_void_p]),
+    "qlora_linear_fwd": (C.c_int, [C.c_void_p, C.c_int64, C.POINTER(qlora_nf4), C.c_void_p, C.c_void_p, C.c_int32,
+                                   C.c_float, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "qlora_linear_bwd": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64, C.POINTER(qlora_nf4), C.c_void_p,
+                                   C.c_void_p, C.c_int32, C.c_float, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                   C.c_size_t, C.c_void_p]),
+    "qlora_profile_enable": (C.c_int, [C.c_int32]),
+    "qlora_profile_read": (C.c_int32, [C.POINTER(qlora_kernel_time), C.c_int32, C.c_int32]),
+}
+
+_lib = None
+
+
+def load(build_if_missing: bool = True) -> C.CDLL:
+    """Load libqlora.so from the package directory (building it first if it is absent)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        if not build_if_missing:
+            raise OSError(f"libqlora.so is not built ({LIB_PATH})")
+        from . import build as _build
+
+        _build.build()
+    lib = C.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib

@@ -1,0 +1,411 @@
+// libqlora host layer: the C ABI declared in include/qlora.h.
+//
+// Validates every argument on the host, carves the caller's workspace, and
+// enqueues the kernels on the caller's stream.  Allocates no device memory.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "qlora.h"
+
+namespace qlora {
+
+// ------------------------------------------------------------------------------------------
+// per-kernel timing (optional)
+// ------------------------------------------------------------------------------------------
+namespace {
+struct ProfRecord {
+  const char* name;
+  hipEvent_t start, stop;
+};
+std::atomic<int> g_prof_enabled{0};
+std::mutex g_prof_mu;
+std::vector<ProfRecord> g_prof_pending;
+struct ProfAgg {
+  std::string name;
+  int64_t launches = 0;
+  double ms = 0.0;
+};
+std::vector<ProfAgg> g_prof_agg;
+}  // namespace
+
+ProfScope::ProfScope(const char* name, hipStream_t s) : slot_(-1), s_(s) {
+  if (!g_prof_enabled.load(std::memory_order_relaxed)) return;
+  ProfRecord rec{name, nullptr, nullptr};
+  if (hipEventCreate(&rec.start) != hipSuccess) return;
+  if (hipEventCreate(&rec.stop) != hipSuccess) {
+    (void)hipEventDestroy(rec.start);
+    return;
+  }
+  (void)hipEventRecord(rec.start, s);
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  slot_ = (int)g_prof_pending.size();
+  g_prof_pending.push_back(rec);
+}
+
+ProfScope::~ProfScope() {
+  if (slot_ < 0) return;
+  hipEvent_t stop;
+  {
+    std::lock_guard<std::mutex> g(g_prof_mu);
+    stop = g_prof_pending[slot_].stop;
+  }
+  (void)hipEventRecord(stop, s_);
+}
+
+}  // namespace qlora
+
+using namespace qlora;
+
+namespace {
+
+constexpr int64_t kMaxDim = int64_t(1) << 31;
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+inline int64_t rank_pad(int64_t r) { return (r + 63) / 64 * 64; }
+
+// Sequential carving of a workspace into 256-byte aligned pieces.
+struct Carve {
+  char* base;
+  size_t off = 0;
+  explicit Carve(void* b) : base(static_cast<char*>(b)) {}
+  template <class T>
+  T* take(size_t count) {
+    off = round_up(off, 256);
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += count * sizeof(T);
+    return p;
+  }
+};
+
+NF4View view_of(const qlora_nf4* w) {
+  NF4View v;
+  v.codes = w->codes;
+  v.absmax = w->absmax;
+  v.c1 = w->c1;
+  v.mu = w->mu;
+  v.dq = w->double_quant;
+  return v;
+}
+
+#define QL_HIP(call)                              \
+  do {                                            \
+    if ((call) != hipSuccess) return QLORA_ERR_HIP; \
+  } while (0)
+
+qlora_status check_nf4(const qlora_nf4* w) {
+  if (!w || !w->codes || !w->absmax) return QLORA_ERR_NULL;
+  if (w->double_quant != 0 && w->double_quant != 1) return QLORA_ERR_UNSUPPORTED;
+  if (w->double_quant && (!w->c1 || !w->mu)) return QLORA_ERR_NULL;
+  if (w->rows < 1 || w->cols < 1 || w->rows >= kMaxDim || w->cols >= kMaxDim) return QLORA_ERR_SHAPE;
+  if (!aligned16(w->codes) || !aligned4(w->absmax) || (w->c1 && !aligned4(w->c1)) || (w->mu && !aligned4(w->mu)))
+    return QLORA_ERR_ALIGN;
+  return QLORA_OK;
+}
+
+qlora_status check_linear(int64_t M, const qlora_nf4* w, int32_t r) {
+  qlora_status st = check_nf4(w);
+  if (st != QLORA_OK) return st;
+  if (M < 0 || M >= (int64_t(1) << 26)) return QLORA_ERR_SHAPE;
+  if (w->cols % 64 != 0 || w->rows % 8 != 0) return QLORA_ERR_SHAPE;
+  if (w->rows > (int64_t(1) << 22) || w->cols > (int64_t(1) << 22)) return QLORA_ERR_SHAPE;
+  if (r < 8 || r > 256 || r % 8 != 0) return QLORA_ERR_UNSUPPORTED;
+  return QLORA_OK;
+}
+
+// ---- workspace layouts ----------------------------------------------------------------------
+struct FwdWs {
+  uint16_t* Ts;
+  float* partial;
+  size_t bytes;
+};
+
+SmallGemm gemm_T(const uint16_t* X, const uint16_t* A, int64_t M, int64_t in, int64_t r) {
+  // T[m][j] = sum_k X[m][k] A[k][j]
+  return SmallGemm{X, in, 1, A, r, 1, M, r, in};
+}
+SmallGemm gemm_G(const uint16_t* dY, const uint16_t* B, int64_t M, int64_t out, int64_t r) {
+  // G[m][j] = sum_n dY[m][n] B[j][n]
+  return SmallGemm{dY, out, 1, B, 1, out, M, r, out};
+}
+SmallGemm gemm_dA(const uint16_t* X, const uint16_t* Gs, int64_t M, int64_t in, int64_t r, int64_t rp) {
+  // dA[i][j] = sum_m X[m][i] Gs[m][j]
+  return SmallGemm{X, 1, in, Gs, rp, 1, in, r, M};
+}
+SmallGemm gemm_dB(const uint16_t* T, int64_t ldT, const uint16_t* dY, int64_t M, int64_t out, int64_t r) {
+  // dB[j][n] = sum_m T[m][j] dY[m][n]
+  return SmallGemm{T, 1, ldT, dY, out, 1, r, out, M};
+}
+
+bool use_gemv(int64_t M) { return M <= 16; }
+
+FwdWs fwd_layout(void* base, int64_t M, int64_t in, int64_t out, int32_t r) {
+  Carve c(base);
+  const int64_t rp = rank_pad(r);
+  FwdWs ws;
+  ws.Ts = c.take<uint16_t>((size_t)std::max<int64_t>(M, 1) * rp);
+  const SmallGemm gt = gemm_T(nullptr, nullptr, std::max<int64_t>(M, 1), in, r);
+  size_t pf = small_gemm_partial_floats(gt);
+  if (use_gemv(M)) pf = std::max(pf, (size_t)gemv_splits(in, out) * (size_t)std::max<int64_t>(M, 1) * out);
+  ws.partial = c.take<float>(pf);
+  ws.bytes = round_up(c.off, 256);
+  return ws;
+}
+
+struct BwdWs {
+  uint16_t* Gs;
+  uint16_t* T;
+  float* partial;
+  size_t bytes;
+};
+
+BwdWs bwd_layout(void* base, int64_t M, int64_t in, int64_t out, int32_t r) {
+  Carve c(base);
+  const int64_t rp = rank_pad(r);
+  const int64_t Mm = std::max<int64_t>(M, 1);
+  BwdWs ws;
+  ws.Gs = c.take<uint16_t>((size_t)Mm * rp);
+  ws.T = c.take<uint16_t>((size_t)Mm * r);
+  size_t pf = small_gemm_partial_floats(gemm_T(nullptr, nullptr, Mm, in, r));
+  pf = std::max(pf, small_gemm_partial_floats(gemm_G(nullptr, nullptr, Mm, out, r)));
+  pf = std::max(pf, small_gemm_partial_floats(gemm_dA(nullptr, nullptr, Mm, in, r, rp)));
+  pf = std::max(pf, small_gemm_partial_floats(gemm_dB(nullptr, r, nullptr, Mm, out, r)));
+  ws.partial = c.take<float>(pf);
+  ws.bytes = round_up(c.off, 256);
+  return ws;
+}
+
+struct QuantWs {
+  unsigned long long* hist;
+  float* absmax;
+  size_t bytes;
+};
+
+QuantWs quant_layout(void* base, int64_t numel) {
+  Carve c(base);
+  QuantWs ws;
+  ws.hist = c.take<unsigned long long>(256);
+  ws.absmax = c.take<float>((size_t)((numel + 63) / 64));
+  ws.bytes = round_up(c.off, 256);
+  return ws;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qlora_status_str(qlora_status s) {
+  switch (s) {
+    case QLORA_OK: return "ok";
+    case QLORA_ERR_NULL: return "required pointer is NULL";
+    case QLORA_ERR_SHAPE: return "size out of range or violates a divisibility rule";
+    case QLORA_ERR_ALIGN: return "pointer not aligned as required";
+    case QLORA_ERR_UNSUPPORTED: return "unsupported option";
+    case QLORA_ERR_WORKSPACE: return "workspace missing or too small";
+    case QLORA_ERR_HIP: return "HIP runtime call or kernel launch failed";
+  }
+  return "unknown status";
+}
+
+const char* qlora_version(void) { return "libqlora 0.1 (gfx950)"; }
+
+qlora_status qlora_nf4_codebook(float levels[16], float thresholds[15]) {
+  if (levels) std::memcpy(levels, nf4_levels_host(), 16 * sizeof(float));
+  if (thresholds) std::memcpy(thresholds, nf4_thresholds_host(), 15 * sizeof(float));
+  return QLORA_OK;
+}
+
+qlora_status qlora_nf4_sizes(int64_t rows, int64_t cols, int32_t dq, size_t* codes_bytes, size_t* absmax_bytes,
+                             size_t* c1_bytes, size_t* mu_bytes) {
+  if (rows < 1 || cols < 1 || rows >= kMaxDim || cols >= kMaxDim) return QLORA_ERR_SHAPE;
+  if (dq != 0 && dq != 1) return QLORA_ERR_UNSUPPORTED;
+  const int64_t numel = rows * cols;
+  const int64_t nblk = (numel + 63) / 64;
+  const int64_t nsup = (nblk + 255) / 256;
+  if (codes_bytes) *codes_bytes = (size_t)nblk * 32;
+  if (absmax_bytes) *absmax_bytes = (size_t)nblk * (dq ? 1 : 4);
+  if (c1_bytes) *c1_bytes = dq ? (size_t)nsup * 4 : 0;
+  if (mu_bytes) *mu_bytes = dq ? 4 : 0;
+  return QLORA_OK;
+}
+
+size_t qlora_quantize_workspace(int64_t rows, int64_t cols, int32_t dq) {
+  if (!dq || rows < 1 || cols < 1 || rows >= kMaxDim || cols >= kMaxDim) return 0;
+  return quant_layout(nullptr, rows * cols).bytes;
+}
+
+size_t qlora_fwd_workspace(int64_t M, int64_t in, int64_t out, int32_t r) {
+  if (M < 0 || in < 64 || out < 8 || r < 8 || r > 256) return 0;
+  return fwd_layout(nullptr, M, in, out, r).bytes;
+}
+
+size_t qlora_bwd_workspace(int64_t M, int64_t in, int64_t out, int32_t r) {
+  if (M < 0 || in < 64 || out < 8 || r < 8 || r > 256) return 0;
+  return bwd_layout(nullptr, M, in, out, r).bytes;
+}
+
+qlora_status qlora_quantize_nf4(const uint16_t* W, int64_t rows, int64_t cols, const qlora_nf4* out, void* ws,
+                                size_t ws_bytes, hipStream_t stream) {
+  if (!W || !out || !out->codes || !out->absmax) return QLORA_ERR_NULL;
+  if (rows < 1 || cols < 1 || rows >= kMaxDim || cols >= kMaxDim) return QLORA_ERR_SHAPE;
+  if (out->rows != rows || out->cols != cols) return QLORA_ERR_SHAPE;
+  const qlora_status st = check_nf4(out);
+  if (st != QLORA_OK) return st;
+  if (!aligned16(W)) return QLORA_ERR_ALIGN;
+  const int64_t numel = rows * cols;
+  const int64_t nblk = (numel + 63) / 64;
+  if (out->double_quant) {
+    const QuantWs need = quant_layout(nullptr, numel);
+    if (!ws || ws_bytes < need.bytes) return QLORA_ERR_WORKSPACE;
+    if (!aligned16(ws)) return QLORA_ERR_ALIGN;
+    const QuantWs q = quant_layout(ws, numel);
+    QL_HIP(launch_fill_u32(reinterpret_cast<uint32_t*>(q.hist), 512, 0u, stream));
+    QL_HIP(launch_quantize(W, numel, out->codes, q.absmax, q.hist, stream));
+    QL_HIP(launch_dq_mean(q.hist, nblk, out->mu, stream));
+    QL_HIP(launch_dq_encode(q.absmax, nblk, out->mu, static_cast<uint8_t*>(out->absmax), out->c1, stream));
+  } else {
+    QL_HIP(launch_quantize(W, numel, out->codes, static_cast<float*>(out->absmax), nullptr, stream));
+  }
+  return QLORA_OK;
+}
+
+qlora_status qlora_dequant(const qlora_nf4* w, uint16_t* W_out, hipStream_t stream) {
+  const qlora_status st = check_nf4(w);
+  if (st != QLORA_OK) return st;
+  if (!W_out) return QLORA_ERR_NULL;
+  if (!aligned16(W_out)) return QLORA_ERR_ALIGN;
+  QL_HIP(launch_dequant(view_of(w), w->rows * w->cols, W_out, stream));
+  return QLORA_OK;
+}
+
+qlora_status qlora_linear_fwd(const uint16_t* X, int64_t M, const qlora_nf4* w, const uint16_t* A,
+                              const uint16_t* B, int32_t r, float scale, uint16_t* Y, uint16_t* T_save, void* ws,
+                              size_t ws_bytes, hipStream_t stream) {
+  qlora_status st = check_linear(M, w, r);
+  if (st != QLORA_OK) return st;
+  // with no tokens the token buffers may be NULL (e.g. empty tensors)
+  if (!A || !B || (M > 0 && (!X || !Y))) return QLORA_ERR_NULL;
+  if ((X && !aligned16(X)) || !aligned16(A) || !aligned16(B) || (Y && !aligned16(Y)) ||
+      (T_save && !aligned16(T_save)))
+    return QLORA_ERR_ALIGN;
+  const int64_t in = w->cols, out = w->rows, rp = rank_pad(r);
+  const FwdWs need = fwd_layout(nullptr, M, in, out, r);
+  if (!ws || ws_bytes < need.bytes) return QLORA_ERR_WORKSPACE;
+  if (!aligned16(ws)) return QLORA_ERR_ALIGN;
+  if (M == 0) return QLORA_OK;
+  const FwdWs L = fwd_layout(ws, M, in, out, r);
+  const NF4View v = view_of(w);
+
+  // T = X A, split over the reduction; Ts = bf16(s T) padded to rp columns; T_save = bf16(T)
+  const SmallGemm gt = gemm_T(X, A, M, in, r);
+  const int st_splits = small_gemm_splits(gt);
+  QL_HIP(launch_small_gemm(gt, L.partial, st_splits, "k_lora_xa", stream));
+  QL_HIP(launch_small_reduce(L.partial, st_splits, M, r, T_save, r, 1.0f, L.Ts, rp, scale, nullptr, 0.0f,
+                             "k_lora_xa_reduce", stream));
+  if (use_gemv(M)) {
+    const int sp = gemv_splits(in, out);
+    QL_HIP(launch_gemv(X, M, in, out, v, L.partial, sp, stream));
+    QL_HIP(launch_gemv_epilogue(L.partial, sp, M, out, L.Ts, rp, B, r, Y, stream));
+  } else {
+    QL_HIP(launch_fwd_gemm(X, M, in, out, v, L.Ts, rp, B, r, Y, stream));
+  }
+  return QLORA_OK;
+}
+
+qlora_status qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, const uint16_t* T_saved, int64_t M,
+                              const qlora_nf4* w, const uint16_t* A, const uint16_t* B, int32_t r, float scale,
+                              uint16_t* dX, float* dA, float* dB, void* ws, size_t ws_bytes, hipStream_t stream) {
+  qlora_status st = check_linear(M, w, r);
+  if (st != QLORA_OK) return st;
+  if (!A || !B || !dA || !dB || (M > 0 && (!dY || !X))) return QLORA_ERR_NULL;
+  if ((dY && !aligned16(dY)) || (X && !aligned16(X)) || !aligned16(A) || !aligned16(B) ||
+      (T_saved && !aligned16(T_saved)) || (dX && !aligned16(dX)) || !aligned4(dA) || !aligned4(dB))
+    return QLORA_ERR_ALIGN;
+  const int64_t in = w->cols, out = w->rows, rp = rank_pad(r);
+  const BwdWs need = bwd_layout(nullptr, M, in, out, r);
+  if (!ws || ws_bytes < need.bytes) return QLORA_ERR_WORKSPACE;
+  if (!aligned16(ws)) return QLORA_ERR_ALIGN;
+  if (M == 0) {
+    QL_HIP(launch_fill_u32(reinterpret_cast<uint32_t*>(dA), in * r, 0u, stream));
+    QL_HIP(launch_fill_u32(reinterpret_cast<uint32_t*>(dB), (int64_t)r * out, 0u, stream));
+    return QLORA_OK;
+  }
+  const BwdWs L = bwd_layout(ws, M, in, out, r);
+  const NF4View v = view_of(w);
+
+  const uint16_t* T = T_saved;
+  if (!T) {
+    const SmallGemm gt = gemm_T(X, A, M, in, r);
+    const int sp = small_gemm_splits(gt);
+    QL_HIP(launch_small_gemm(gt, L.partial, sp, "k_lora_xa", stream));
+    QL_HIP(launch_small_reduce(L.partial, sp, M, r, L.T, r, 1.0f, nullptr, 0, 0.0f, nullptr, 0.0f,
+                               "k_lora_xa_reduce", stream));
+    T = L.T;
+  }
+  // Gs = bf16(s dY B^T), padded to rp columns
+  const SmallGemm gg = gemm_G(dY, B, M, out, r);
+  const int sg = small_gemm_splits(gg);
+  QL_HIP(launch_small_gemm(gg, L.partial, sg, "k_lora_dyb", stream));
+  QL_HIP(launch_small_reduce(L.partial, sg, M, r, nullptr, 0, 0.0f, L.Gs, rp, scale, nullptr, 0.0f,
+                             "k_lora_dyb_reduce", stream));
+  if (dX) QL_HIP(launch_dx_gemm(dY, M, in, out, v, L.Gs, rp, A, r, dX, stream));
+  // dA = X^T Gs
+  const SmallGemm ga = gemm_dA(X, L.Gs, M, in, r, rp);
+  const int sa = small_gemm_splits(ga);
+  QL_HIP(launch_small_gemm(ga, L.partial, sa, "k_lora_da", stream));
+  QL_HIP(launch_small_reduce(L.partial, sa, in, r, nullptr, 0, 0.0f, nullptr, 0, 0.0f, dA, 1.0f, "k_lora_da_reduce",
+                             stream));
+  // dB = s T^T dY
+  const SmallGemm gb = gemm_dB(T, r, dY, M, out, r);
+  const int sb = small_gemm_splits(gb);
+  QL_HIP(launch_small_gemm(gb, L.partial, sb, "k_lora_db", stream));
+  QL_HIP(launch_small_reduce(L.partial, sb, r, out, nullptr, 0, 0.0f, nullptr, 0, 0.0f, dB, scale, "k_lora_db_reduce",
+                             stream));
+  return QLORA_OK;
+}
+
+qlora_status qlora_profile_enable(int32_t enable) {
+  g_prof_enabled.store(enable ? 1 : 0);
+  return QLORA_OK;
+}
+
+int32_t qlora_profile_read(qlora_kernel_time* outp, int32_t max_entries, int32_t reset) {
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  for (auto& rec : g_prof_pending) {
+    float ms = 0.0f;
+    if (hipEventSynchronize(rec.stop) == hipSuccess && hipEventElapsedTime(&ms, rec.start, rec.stop) == hipSuccess) {
+      auto it = std::find_if(g_prof_agg.begin(), g_prof_agg.end(),
+                             [&](const ProfAgg& a) { return a.name == rec.name; });
+      if (it == g_prof_agg.end()) {
+        g_prof_agg.push_back(ProfAgg{rec.name, 0, 0.0});
+        it = g_prof_agg.end() - 1;
+      }
+      it->launches += 1;
+      it->ms += ms;
+    }
+    (void)hipEventDestroy(rec.start);
+    (void)hipEventDestroy(rec.stop);
+  }
+  g_prof_pending.clear();
+  int32_t n = 0;
+  for (const auto& a : g_prof_agg) {
+    if (n >= max_entries || !outp) break;
+    std::memset(&outp[n], 0, sizeof(qlora_kernel_time));
+    std::strncpy(outp[n].name, a.name.c_str(), sizeof(outp[n].name) - 1);
+    outp[n].launches = a.launches;
+    outp[n].total_ms = a.ms;
+    ++n;
+  }
+  if (reset) g_prof_agg.clear();
+  return n;
+}
+
+}  // extern "C"

@@ -1,0 +1,87 @@
+// Host computation of the NF4 levels and encoder thresholds.
+//
+// Procedure ("QLoRA: Efficient Finetuning of Quantized LLMs", section
+// "NormalFloat: 4 bits for a bell curve", the code-point listing): take
+// standard-normal quantiles at 9 probabilities evenly spaced from the offset
+// 0.9677083 down to 1/2 and keep the first 8 (positive levels); take 8 such
+// points for the negative side, keep the first 7 and negate; add an exact zero;
+// sort; divide by the largest magnitude so the ends are exactly -1 and +1.
+//
+// The quantile function is this file's own: Newton's method on the upper tail
+// Q(x) = erfc(x / sqrt 2) / 2 = 1 - p, started at x = 0.  Q is convex and
+// decreasing for x >= 0 and every probability used is in (1/2, 1), so the
+// iterates increase monotonically to the root.  The probabilities are formed the
+// way an evenly spaced grid is usually formed, start + i * step with
+// step = (stop - start) / (num - 1), in float64.
+//
+// Built with -ffp-contract=off so no multiply-add is fused.
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+namespace qlora {
+
+namespace {
+
+constexpr double kOffset = 0.9677083;
+
+double upper_tail_quantile(double q /* = 1 - p, in (0, 1/2) */) {
+  const double inv_sqrt2 = 0.70710678118654752440;
+  const double inv_sqrt_2pi = 0.39894228040143267794;
+  double x = 0.0;
+  for (int it = 0; it < 200; ++it) {
+    double tail = 0.5 * std::erfc(x * inv_sqrt2);
+    double dens = inv_sqrt_2pi * std::exp(-0.5 * x * x);
+    double step = (tail - q) / dens;
+    double nx = x + step;
+    if (!(nx > x)) break;   // converged: no further increase representable
+    x = nx;
+  }
+  return x;
+}
+
+double quantile(double p) { return upper_tail_quantile(1.0 - p); }
+
+float round_down_f32(double v) {
+  float f = (float)v;
+  if ((double)f > v) f = std::nextafterf(f, -INFINITY);
+  return f;
+}
+
+struct Codebook {
+  float level[16];
+  float thr[15];
+  Codebook() {
+    double v[16];
+    int n = 0;
+    const double step_pos = (0.5 - kOffset) / 8.0;   // 9 points, last (1/2) dropped
+    for (int i = 0; i < 8; ++i) v[n++] = quantile((double)i * step_pos + kOffset);
+    const double step_neg = (0.5 - kOffset) / 7.0;   // 8 points, last dropped
+    for (int i = 0; i < 7; ++i) v[n++] = -quantile((double)i * step_neg + kOffset);
+    v[n++] = 0.0;
+    // sort ascending (insertion sort, 16 values)
+    for (int i = 1; i < 16; ++i) {
+      double key = v[i];
+      int j = i - 1;
+      while (j >= 0 && v[j] > key) { v[j + 1] = v[j]; --j; }
+      v[j + 1] = key;
+    }
+    double mx = 0.0;
+    for (int i = 0; i < 16; ++i) mx = std::fmax(mx, std::fabs(v[i]));
+    for (int i = 0; i < 16; ++i) level[i] = (float)(v[i] / mx);
+    for (int k = 0; k < 15; ++k) thr[k] = round_down_f32(((double)level[k] + (double)level[k + 1]) * 0.5);
+  }
+};
+
+}  // namespace
+
+static const Codebook& codebook() {
+  static const Codebook cb;   // computed once; thread-safe initialization
+  return cb;
+}
+
+const float* nf4_levels_host() { return codebook().level; }
+
+const float* nf4_thresholds_host() { return codebook().thr; }
+
+}  // namespace qlora

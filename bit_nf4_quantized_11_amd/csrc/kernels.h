@@ -1,0 +1,74 @@
+// Internal launch interface between the host layer (api.cpp) and the kernels.
+// Every launcher validates nothing: the host layer has already checked shapes,
+// pointers and workspace.  All return hipGetLastError() of their launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace qlora {
+
+// Host-side NF4 table (computed once, see codebook.cpp).
+const float* nf4_levels_host();
+const float* nf4_thresholds_host();
+NF4Table nf4_table();
+
+// Optional per-launch timing (api.cpp).
+struct ProfScope {
+  ProfScope(const char* name, hipStream_t s);
+  ~ProfScope();
+  int slot_;
+  hipStream_t s_;
+};
+
+// ---- quantize / dequantize (quant.hip) --------------------------------------------------
+hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
+hipError_t launch_quantize(const uint16_t* W, int64_t numel, uint8_t* codes, float* absmax_f32,
+                           unsigned long long* hist, hipStream_t s);
+hipError_t launch_dq_mean(const unsigned long long* hist, int64_t nblk, float* mu, hipStream_t s);
+hipError_t launch_dq_encode(const float* absmax_f32, int64_t nblk, const float* mu, uint8_t* c2, float* c1,
+                            hipStream_t s);
+hipError_t launch_dequant(const NF4View& w, int64_t numel, uint16_t* out, hipStream_t s);
+
+// ---- small rank-r products (lora.hip) ----------------------------------------------------
+// partial[split][I][J] = sum_{k in split} A(i,k) B(k,j); A(i,k) = A[i*a_si + k*a_sk] (one of the two
+// strides is 1), B(k,j) = B[k*b_sk + j*b_sj] (one of the two strides is 1).
+struct SmallGemm {
+  const uint16_t* A;
+  int64_t a_si, a_sk;
+  const uint16_t* B;
+  int64_t b_sk, b_sj;
+  int64_t I, J, K;
+};
+int small_gemm_splits(const SmallGemm& g);
+size_t small_gemm_partial_floats(const SmallGemm& g);
+hipError_t launch_small_gemm(const SmallGemm& g, float* partial, int splits, const char* name, hipStream_t s);
+// out_a[i*lda + j] = bf16(scale_a * sum)   (j < J; NULL to skip)
+// out_b[i*ldb + j] = bf16(scale_b * sum)   (j < J), 0 for J <= j < ldb  (NULL to skip)
+// out_f[i*J + j]   = scale_f * sum         (NULL to skip)
+hipError_t launch_small_reduce(const float* partial, int splits, int64_t I, int64_t J, uint16_t* out_a, int64_t lda,
+                               float scale_a, uint16_t* out_b, int64_t ldb, float scale_b, float* out_f,
+                               float scale_f, const char* name, hipStream_t s);
+
+// ---- fused forward, large M (fwd_gemm.hip) ------------------------------------------------
+// Y[M][N] = bf16( X[M][K] deq(W)^T + Ts[M][rp] Bt ), Bt(j, n) = B[j][n] for j < r else 0.
+hipError_t launch_fwd_gemm(const uint16_t* X, int64_t M, int64_t K, int64_t N, const NF4View& w,
+                           const uint16_t* Ts, int64_t rp, const uint16_t* B, int64_t r, uint16_t* Y,
+                           hipStream_t s);
+
+// ---- fused forward, skinny M <= 16 (gemv.hip) ---------------------------------------------
+int gemv_splits(int64_t K, int64_t N);
+hipError_t launch_gemv(const uint16_t* X, int64_t M, int64_t K, int64_t N, const NF4View& w, float* partial,
+                       int splits, hipStream_t s);
+hipError_t launch_gemv_epilogue(const float* partial, int splits, int64_t M, int64_t N, const uint16_t* Ts,
+                                int64_t rp, const uint16_t* B, int64_t r, uint16_t* Y, hipStream_t s);
+
+// ---- backward dX (dx_gemm.hip) --------------------------------------------------------------
+// dX[M][K] = bf16( dY[M][N] deq(W) + Gs[M][rp] A^T ), A [K][r].
+hipError_t launch_dx_gemm(const uint16_t* dY, int64_t M, int64_t K, int64_t N, const NF4View& w,
+                          const uint16_t* Gs, int64_t rp, const uint16_t* A, int64_t r, uint16_t* dX,
+                          hipStream_t s);
+
+}  // namespace qlora

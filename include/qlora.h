@@ -1,0 +1,171 @@
+/*
+ * libqlora -- QLoRA linear layer for AMD Instinct MI355X (gfx950).
+ *
+ * A frozen bf16 weight is stored as 4-bit NormalFloat (NF4) codes with one
+ * absmax constant per 64-weight block; the constants are themselves quantized
+ * to 8-bit floats in groups of 256 with one fp32 scale per group ("double
+ * quantization").  The layer computes, in bf16 with fp32 accumulation,
+ *
+ *     Y  = X deq(W)^T + s (X A) B
+ *     dX = dY deq(W) + s (dY B^T) A^T,   dA = s X^T (dY B^T),   dB = s (X A)^T dY
+ *
+ * with no gradient for the frozen W.  Sources ("QLoRA: Efficient Finetuning of
+ * Quantized LLMs", intuitivepapers.ai): sections "Quantize in blocks, not all
+ * at once", "NormalFloat: 4 bits for a bell curve", "Double quantization" and
+ * "The QLoRA layer, end to end" (the one-layer code listing).  The review page
+ * "QLoRA Review: 4-Bit Finetuning for 65B Models on One GPU", section "The
+ * Gradient Flow Trick", states the same layer with s = 1.
+ *
+ * Conventions for every call
+ *   - bf16 tensors are passed as uint16_t bit patterns; all tensors are dense
+ *     row-major.  W is [rows = out][cols = in] (the layout of a torch Linear
+ *     weight); A is [in][r]; B is [r][out]; X is [M][in]; Y, dY are [M][out].
+ *   - Device pointers unless stated otherwise.  The caller owns every buffer;
+ *     the library never allocates or frees device memory and keeps no state
+ *     other than read-only constants, so concurrent calls on different streams
+ *     are safe when they write disjoint buffers.
+ *   - Calls are asynchronous on `stream`.  QLORA_OK means the arguments were
+ *     valid and every launch was accepted, not that the kernels finished.
+ *   - Arguments are validated on the host before any launch; on error nothing
+ *     is launched and the status says why.  The library never prints or aborts.
+ */
+#ifndef QLORA_H
+#define QLORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QLORA_OK = 0,
+  QLORA_ERR_NULL = 1,        /* a required pointer is NULL                                   */
+  QLORA_ERR_SHAPE = 2,       /* a size is out of range or violates a divisibility rule        */
+  QLORA_ERR_ALIGN = 3,       /* a pointer is not aligned as required (16 bytes)               */
+  QLORA_ERR_UNSUPPORTED = 4, /* a valid but unsupported option (rank, format flag)            */
+  QLORA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than the matching *_workspace query */
+  QLORA_ERR_HIP = 6          /* a HIP runtime call or kernel launch failed                    */
+} qlora_status;
+
+/* Quantized weight: caller-owned views of device buffers.
+ *   codes  : 32 * nblk bytes.  The flattened row-major weight is cut into blocks
+ *            of 64, each stored whole in 32 bytes; inside a block the group of 8
+ *            elements 8g..8g+7 sits in bytes 4g..4g+3, and byte i of a group holds
+ *            element i in bits 3..0 and element i+4 in bits 7..4.  Positions past
+ *            the end of the tensor hold code 7 (the exact zero).
+ *   absmax : double_quant = 1 -> nblk bytes, FP8 E4M3 code of (absmax_b - mu) / c1
+ *            double_quant = 0 -> nblk floats, the block absmax itself
+ *            (nblk = ceil(rows*cols / 64))
+ *   c1     : double_quant = 1 -> nsup floats, one scale per 256 blocks
+ *            (nsup = ceil(nblk / 256)); unused (may be NULL) otherwise
+ *   mu     : double_quant = 1 -> 1 float, the mean of all block absmax values;
+ *            unused (may be NULL) otherwise
+ * Block scale used by dequant ("doubleDequant", inner step first):
+ *   s'_b = fl32(fl32(e4m3(absmax_b) * c1_{b/256}) + mu)   (double_quant = 1)
+ *   s'_b = absmax_b                                       (double_quant = 0)
+ * Dequantized weight: bf16_RNE(fl32(level[code] * s'_b)).                        */
+typedef struct {
+  int64_t rows;
+  int64_t cols;
+  int32_t double_quant;
+  int32_t reserved;
+  uint8_t* codes;
+  void* absmax;
+  float* c1;
+  float* mu;
+} qlora_nf4;
+
+/* Human-readable name of a status code (static string). */
+const char* qlora_status_str(qlora_status s);
+
+/* Library version string (static). */
+const char* qlora_version(void);
+
+/* Host only.  The 16 NF4 levels (fp32, ascending; index 7 is the exact zero)
+ * and the 15 decision thresholds the encoder uses: code = #{k : x > t_k}, with
+ * t_k the largest fp32 not above the midpoint of levels k and k+1, which gives
+ * the nearest level with ties to the lower index.  The levels follow the
+ * procedure in "NormalFloat: 4 bits for a bell curve": standard-normal
+ * quantiles with the tails pulled in by the offset 0.9677083, 8 positive, 7
+ * negative and an exact zero, divided by the largest magnitude.  Computed once
+ * in float64 by the library's own inverse normal CDF, then rounded to fp32.
+ * Either pointer may be NULL.                                                   */
+qlora_status qlora_nf4_codebook(float levels[16], float thresholds[15]);
+
+/* Host only.  Bytes of each buffer of a quantized [rows][cols] weight
+ * ("Double quantization": 4-bit codes, 8-bit constants per 64, one fp32 per
+ * 256 constants, one fp32 mean).  rows, cols >= 1.  Any output may be NULL.   */
+qlora_status qlora_nf4_sizes(int64_t rows, int64_t cols, int32_t double_quant, size_t* codes_bytes,
+                             size_t* absmax_bytes, size_t* c1_bytes, size_t* mu_bytes);
+
+/* Host only.  Workspace bytes each call needs (0 means none; pass ws = NULL). */
+size_t qlora_quantize_workspace(int64_t rows, int64_t cols, int32_t double_quant);
+size_t qlora_fwd_workspace(int64_t M, int64_t in_features, int64_t out_features, int32_t r);
+size_t qlora_bwd_workspace(int64_t M, int64_t in_features, int64_t out_features, int32_t r);
+
+/* Blockwise NF4 quantization of W [rows][cols] bf16 into `out` (whose rows,
+ * cols, double_quant and buffers the caller sets; see qlora_nf4_sizes).
+ * Per 64-block: a = max|w| (a below 2^-126 makes the block all code 7 with
+ * a = 0); x = fl32(w * fl32(1/a)); code = nearest NF4 level, ties to the lower
+ * index ("Quantize in blocks, not all at once"; "NormalFloat").  With
+ * double_quant: mu = fl32(S / nblk), S the exact sum of all a rounded once to
+ * float64; per group of 256 blocks m = max|fl32(a - mu)|, c1 = fl32(m / 448)
+ * (c1 below 2^-126 -> c1 = 0 and codes 0), c2 = E4M3_RNE(fl32(fl32(a - mu) *
+ * fl32(1/c1))) ("Double quantization").  Results are deterministic.
+ * Any rows, cols >= 1 (a partial last block and group are allowed).
+ * Requires: W and out->codes 16-byte aligned; W finite.                          */
+qlora_status qlora_quantize_nf4(const uint16_t* W, int64_t rows, int64_t cols, const qlora_nf4* out, void* ws,
+                                size_t ws_bytes, hipStream_t stream);
+
+/* doubleDequant of a whole weight into W_out [rows][cols] bf16 (bit-exact with
+ * the definition in the qlora_nf4 comment).  W_out 16-byte aligned.            */
+qlora_status qlora_dequant(const qlora_nf4* w, uint16_t* W_out, hipStream_t stream);
+
+/* Forward ("The QLoRA layer, end to end"):
+ *   Y [M][out] = bf16( X [M][in] deq(W)^T + scale * T B ),  T = X A  [M][r]
+ * The dequantized weight is formed on the fly and never stored.  T is rounded
+ * to bf16 before its product with B.  If T_save is not NULL, bf16(T) is written
+ * there [M][r] for the backward.  M >= 0; M = 0 is a no-op, and then the token
+ * buffers X, Y and T_save may be NULL.
+ * Requires: in % 64 == 0, out % 8 == 0, r % 8 == 0, 8 <= r <= 256; all pointers
+ * 16-byte aligned; ws of qlora_fwd_workspace(M, in, out, r) bytes.            */
+qlora_status qlora_linear_fwd(const uint16_t* X, int64_t M, const qlora_nf4* w, const uint16_t* A,
+                              const uint16_t* B, int32_t r, float scale, uint16_t* Y, uint16_t* T_save,
+                              void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Backward ("The QLoRA layer, end to end"; no gradient for W):
+ *   G  = dY B^T                         [M][r]   (rounded to bf16 after scaling by `scale`)
+ *   dX = bf16( dY deq(W) + scale G A^T ) [M][in] (skipped if dX is NULL)
+ *   dA = scale X^T G                    [in][r]  fp32, overwritten
+ *   dB = scale T^T dY                   [r][out] fp32, overwritten
+ * T_saved is bf16(X A) from the forward, or NULL to recompute it.  With M = 0,
+ * dA and dB are set to zero and dY, X, T_saved, dX may be NULL.  Same shape and alignment rules as the forward;
+ * ws of qlora_bwd_workspace(M, in, out, r) bytes.                              */
+qlora_status qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, const uint16_t* T_saved, int64_t M,
+                              const qlora_nf4* w, const uint16_t* A, const uint16_t* B, int32_t r, float scale,
+                              uint16_t* dX, float* dA, float* dB, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Optional per-kernel timing, for benchmarking.  While enabled, every kernel
+ * launch of this library is bracketed by HIP events on its stream.
+ * qlora_profile_read synchronizes those events and returns, per kernel name,
+ * the launch count and total milliseconds since the last reset; returns the
+ * number of entries written (at most max_entries).  Not thread-safe against
+ * concurrent launches from other threads while reading.                        */
+typedef struct {
+  char name[48];
+  int64_t launches;
+  double total_ms;
+} qlora_kernel_time;
+
+qlora_status qlora_profile_enable(int32_t enable);
+int32_t qlora_profile_read(qlora_kernel_time* out, int32_t max_entries, int32_t reset);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLORA_H */

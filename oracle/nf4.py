@@ -31,8 +31,10 @@ Readings where the pages leave a step open (each is listed in the design notes):
   R4  a block whose absmax is below the smallest normal fp32 (2^-126) is a zero
       block: stored absmax 0, every code 7 (the exact zero);
   R5  W is the [out][in] row-major weight; blocks run along the flattened array;
-  R6  element 2i goes to bits 7..4 of byte i, element 2i+1 to bits 3..0; a final
-      odd element is padded with code 7;
+  R6  codes are stored as whole 64-blocks of 32 bytes; inside a block, the
+      8-element group g (elements 8g..8g+7) sits in bytes 4g..4g+3, byte i of a
+      group holding element i in bits 3..0 and element i+4 in bits 7..4;
+      positions past the end of the tensor hold code 7 (the exact zero);
   R7  the 8-bit float is OCP FP8 E4M3 (max 448), round to nearest even, the
       group's largest centered magnitude mapped to 448;
   R8  one mean per tensor, mu = fl32(S / nblk) with S the correctly rounded
@@ -188,18 +190,21 @@ def codes_for_blocks(w_bits: np.ndarray, absmax: np.ndarray, block_ids: np.ndarr
 
 
 def pack_nibbles(codes: np.ndarray, numel: int) -> np.ndarray:
-    """Two codes per byte, element 2i in the high nibble (reading R6); ceil(numel/2) bytes."""
-    c = np.full(2 * (-(-numel // 2)), ZERO_CODE, dtype=np.uint8)
+    """Codes -> 32 bytes per 64-block in the layout of reading R6; returns nblk*32 bytes."""
+    nblk = num_blocks(numel)
+    c = np.full(nblk * BLOCK, ZERO_CODE, dtype=np.uint8)
     c[:numel] = np.ravel(codes)[:numel]
-    return ((c[0::2] << 4) | c[1::2]).astype(np.uint8)
+    g = c.reshape(-1, 8)                                   # one row per 8-element group
+    return (g[:, 0:4] | (g[:, 4:8] << 4)).astype(np.uint8).reshape(-1)
 
 
 def unpack_nibbles(packed: np.ndarray, numel: int) -> np.ndarray:
-    p = np.asarray(packed, dtype=np.uint8)
-    out = np.empty(2 * p.size, dtype=np.uint8)
-    out[0::2] = p >> 4
-    out[1::2] = p & 0x0F
-    return out[:numel]
+    """Inverse of pack_nibbles; returns the first numel codes."""
+    p = np.asarray(packed, dtype=np.uint8).reshape(-1, 4)
+    out = np.empty((p.shape[0], 8), dtype=np.uint8)
+    out[:, 0:4] = p & 0x0F
+    out[:, 4:8] = p >> 4
+    return out.reshape(-1)[:numel]
 
 
 # ----------------------------------------------------------------------------------------------
@@ -323,8 +328,8 @@ def storage_bytes(numel: int, double_quant: bool = True) -> dict:
     """Bytes of each stored buffer: codes, block constants, second-level scales, mean."""
     nblk = num_blocks(numel)
     if double_quant:
-        return {"codes": -(-numel // 2), "absmax": nblk, "c1": 4 * num_super(nblk), "mu": 4}
-    return {"codes": -(-numel // 2), "absmax": 4 * nblk, "c1": 0, "mu": 0}
+        return {"codes": 32 * nblk, "absmax": nblk, "c1": 4 * num_super(nblk), "mu": 4}
+    return {"codes": 32 * nblk, "absmax": 4 * nblk, "c1": 0, "mu": 0}
 
 
 def constant_bits_per_param(numel: int, double_quant: bool = True) -> float:

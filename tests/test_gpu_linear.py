@@ -1,0 +1,173 @@
+"""GPU parity of the fused QLoRA linear forward/backward against the float64 oracle
+(tolerances in helpers.py), on small shapes spanning several tiles with ragged
+tails, and on the full-size configurations."""
+import numpy as np
+import pytest
+import torch
+
+import bit_nf4_quantized_11_amd as Q
+import workloads
+from helpers import assert_close, bf16_f64, dev_bf16, host, host_u16, log, require_gpu
+from oracle import linear, nf4
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_weight(w_u16, shape, dq=True):
+    q = nf4.quantize(w_u16, double_quant=dq)
+    return nf4.dequantize(q, shape)
+
+
+def _run(inp: workloads.LinearInputs, dq=True, save_T=True, need_dX=True, backward=True):
+    require_gpu()
+    lin = inp.spec
+    W = dev_bf16(inp.W)
+    q = Q.qlora_quantize_nf4(W, double_quant=dq)
+    X, A, B = dev_bf16(inp.X), dev_bf16(inp.A), dev_bf16(inp.B)
+    Y, T = Q.qlora_linear_fwd(X, q, A, B, lin.scale, save_T=save_T)
+    out = {"Y": Y, "T": T}
+    if backward:
+        dY = dev_bf16(inp.dY)
+        dX, dA, dB = Q.qlora_linear_bwd(dY, X, T if save_T else None, q, A, B, lin.scale, need_dX=need_dX)
+        out.update(dX=dX, dA=dA, dB=dB)
+    torch.cuda.synchronize()
+    return out
+
+
+def _check_full(inp, dq=True, save_T=True, need_dX=True, backward=True, label=""):
+    lin = inp.spec
+    log("linear", label, f"M={lin.M} in={lin.d_in} out={lin.d_out} r={lin.r} s={lin.scale}")
+    g = _run(inp, dq, save_T, need_dX, backward)
+    Wd = _oracle_weight(inp.W, (lin.d_out, lin.d_in), dq)
+    y, t = linear.forward(inp.X, Wd, inp.A, inp.B, lin.scale)
+    errs = {"Y": assert_close(host(g["Y"].float()), y, f"{label} Y")}
+    if save_T:
+        errs["T"] = assert_close(host(g["T"].float()), t, f"{label} T")
+    if backward:
+        dx, da, db = linear.backward(inp.dY, inp.X, Wd, inp.A, inp.B, lin.scale)
+        if need_dX:
+            errs["dX"] = assert_close(host(g["dX"].float()), dx, f"{label} dX")
+        errs["dA"] = assert_close(host(g["dA"]), da, f"{label} dA")
+        errs["dB"] = assert_close(host(g["dB"]), db, f"{label} dB")
+    log("  errors (max-rel, fro-rel):", {k: (f"{a:.2e}", f"{b:.2e}") for k, (a, b) in errs.items()})
+    return g
+
+
+def test_c1_config():
+    lin = workloads.CONFIGS[1].linears[0]
+    _check_full(workloads.linear_inputs(1, lin), label="C1")
+
+
+SMALL = [
+    # (M, in, out, r, alpha) -- several tiles and ragged tails of each dimension
+    (100, 320, 200, 8, 16.0),      # ragged M, in not a multiple of the 128 dX tile, out not of the 128 fwd tile
+    (17, 256, 264, 16, 32.0),      # just above the skinny-M threshold
+    (300, 128, 512, 72, 16.0),     # rank padded to 128
+    (513, 1024, 1024, 64, 16.0),   # 3 token tiles, 8 feature tiles
+    (1, 64, 8, 8, 16.0),           # smallest legal layer
+    (16, 1024, 1536, 64, 16.0),    # skinny path, several splits
+    (4, 2048, 1000, 8, 16.0),      # skinny, ragged feature groups
+    (1, 4096, 4104, 256, 8.0),     # skinny, largest rank
+    (256, 768, 384, 256, 16.0),    # exact tiles, largest rank
+]
+
+
+@pytest.mark.parametrize("M,din,dout,r,alpha", SMALL)
+def test_small_shapes(M, din, dout, r, alpha):
+    inp = workloads.custom_linear(M, din, dout, r, seed=M * 7 + din + dout + r, alpha=alpha)
+    _check_full(inp, label=f"small{(M, din, dout, r)}")
+
+
+def test_options_no_double_quant_recompute_T_skip_dX():
+    inp = workloads.custom_linear(200, 512, 256, 16, seed=3)
+    _check_full(inp, dq=False, label="no-dq")
+    _check_full(inp, save_T=False, label="recompute-T")
+    _check_full(inp, need_dX=False, label="no-dX")
+
+
+def test_empty_token_batch():
+    require_gpu()
+    inp = workloads.custom_linear(1, 256, 128, 8, seed=4)
+    q = Q.qlora_quantize_nf4(dev_bf16(inp.W))
+    X = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    A, B = dev_bf16(inp.A), dev_bf16(inp.B)
+    Y, T = Q.qlora_linear_fwd(X, q, A, B, 2.0)
+    dA = torch.full((256, 8), 7.0, device="cuda")
+    dB = torch.full((8, 128), 7.0, device="cuda")
+    dY = torch.empty((0, 128), dtype=torch.bfloat16, device="cuda")
+    dX, dA, dB = Q.qlora_linear_bwd(dY, X, T, q, A, B, 2.0, dA=dA, dB=dB)
+    torch.cuda.synchronize()
+    assert Y.shape == (0, 128) and dX.shape == (0, 256)
+    assert torch.all(dA == 0) and torch.all(dB == 0)
+
+
+def test_zero_weight_and_zero_adapter():
+    require_gpu()
+    inp = workloads.custom_linear(64, 256, 256, 8, seed=5)
+    zero_w = workloads.LinearInputs(np.zeros_like(inp.W), inp.A, inp.B, inp.X, inp.dY, inp.spec)
+    g = _check_full(zero_w, label="zero-W")
+    y_ref = inp.spec.scale * (bf16_f64(inp.X) @ bf16_f64(inp.A)) @ bf16_f64(inp.B)
+    assert_close(host(g["Y"].float()), y_ref, "zero-W Y closed form")
+    zero_a = workloads.LinearInputs(inp.W, np.zeros_like(inp.A), inp.B, inp.X, inp.dY, inp.spec)
+    g = _run(zero_a)
+    assert torch.all(g["dB"] == 0)
+
+
+def test_forward_backward_deterministic():
+    inp = workloads.custom_linear(600, 1024, 768, 64, seed=6)
+    a = _run(inp)
+    b = _run(inp)
+    for k in ("Y", "T", "dX", "dA", "dB"):
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_c2_full():
+    lin = workloads.CONFIGS[2].linears[0]
+    _check_full(workloads.linear_inputs(2, lin), label="C2")
+
+
+def _check_sampled(cfg, lin, rows, backward=True, layer=0):
+    """Full-size run; Y/dX checked on sampled token rows, dA/dB in full."""
+    inp = workloads.linear_inputs(cfg, lin, layer=layer)
+    log("linear sampled", lin.name, f"M={lin.M} in={lin.d_in} out={lin.d_out}")
+    g = _run(inp, backward=backward)
+    Wd = _oracle_weight(inp.W, (lin.d_out, lin.d_in))
+    rows = np.asarray(rows)
+    y = linear.forward_rows(inp.X, Wd, inp.A, inp.B, lin.scale, rows)
+    assert_close(host(g["Y"].float())[rows], y, f"{lin.name} Y rows")
+    if backward:
+        dx = linear.backward_dx_rows(inp.dY, Wd, inp.A, inp.B, lin.scale, rows)
+        assert_close(host(g["dX"].float())[rows], dx, f"{lin.name} dX rows")
+        x, a, b, dy = bf16_f64(inp.X), bf16_f64(inp.A), bf16_f64(inp.B), bf16_f64(inp.dY)
+        gm = dy @ b.T
+        assert_close(host(g["dA"]), lin.scale * (x.T @ gm), f"{lin.name} dA")
+        assert_close(host(g["dB"]), lin.scale * ((x @ a).T @ dy), f"{lin.name} dB")
+
+
+@pytest.mark.parametrize("which", [0, 1])
+def test_c3_full_sampled(which):
+    lin = workloads.CONFIGS[3].linears[which]
+    rows = np.random.default_rng(which).choice(lin.M, 192, replace=False)
+    _check_sampled(3, lin, rows)
+
+
+@pytest.mark.parametrize("idx", range(6))
+def test_c4_skinny_full(idx):
+    """Skinny forward at 65B shapes; every token row checked, on sampled output columns."""
+    require_gpu()
+    lin = workloads.CONFIGS[4].linears[idx]
+    inp = workloads.linear_inputs(4, lin)
+    log("skinny", lin.name, f"M={lin.M} in={lin.d_in} out={lin.d_out}")
+    g = _run(inp, backward=False)
+    cols = np.sort(np.random.default_rng(idx).choice(lin.d_out, 96, replace=False))
+    # oracle weight rows for the sampled columns only (the constants need every block)
+    absmax = nf4.blockwise_absmax(inp.W)
+    c2, c1, mu = nf4.double_quantize(absmax)
+    scales = nf4.block_scales_dq(c2, c1, mu)
+    nkb = lin.d_in // 64
+    blocks = (cols[:, None] * nkb + np.arange(nkb)[None, :]).reshape(-1)
+    codes = nf4.codes_for_blocks(inp.W, absmax, blocks).reshape(-1)
+    wrows = nf4.dequantize_codes(codes, scales[blocks]).reshape(cols.size, lin.d_in)
+    x, a, b = bf16_f64(inp.X), bf16_f64(inp.A), bf16_f64(inp.B)
+    y = x @ bf16_f64(wrows).T + lin.scale * (x @ a) @ b[:, cols]
+    assert_close(host(g["Y"].float())[:, cols], y, f"{lin.name} Y cols")

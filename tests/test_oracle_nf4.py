@@ -190,11 +190,17 @@ def test_zero_and_subnormal_blocks():
     assert np.array_equal(d[128:192], w[128:192])
 
 
-def test_pack_order_and_odd_tail():
-    codes = np.array([1, 2, 3, 4, 5], dtype=np.uint8)
-    p = nf4.pack_nibbles(codes, 5)
-    assert list(p) == [0x12, 0x34, 0x57]
-    assert list(nf4.unpack_nibbles(p, 5)) == [1, 2, 3, 4, 5]
+def test_pack_layout_and_ragged_tail():
+    codes = np.arange(16, dtype=np.uint8) % 16
+    p = nf4.pack_nibbles(codes, 16)
+    assert p.size == 32                      # one whole block
+    # group 0: bytes hold (e0,e4), (e1,e5), (e2,e6), (e3,e7) as low/high nibbles
+    assert list(p[:8]) == [0x40, 0x51, 0x62, 0x73, 0xC8, 0xD9, 0xEA, 0xFB]
+    assert np.all(p[8:] == 0x77)             # padding is the exact-zero code
+    assert np.array_equal(nf4.unpack_nibbles(p, 16), codes)
+    rng = np.random.default_rng(2)
+    c = rng.integers(0, 16, 201).astype(np.uint8)
+    assert np.array_equal(nf4.unpack_nibbles(nf4.pack_nibbles(c, 201), 201), c)
 
 
 # ------------------------------------------------------------------------------------------
