@@ -55,8 +55,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemv", action="store_true")
     ap.add_argument("--gemv-iters", type=int, default=50)
-    ap.add_argument("--only", choices=["all", "headline", "gemv"], default="all",
-                    help="restrict the run (for profiling single kernels)")
+    ap.add_argument("--only", choices=["all", "headline", "gemv", "copy"], default="all",
+                    help="restrict the run (for profiling single kernels); 'copy' runs a plain device copy of "
+                         "known size, the reference for scaling hardware byte counters")
     return ap.parse_args()
 
 
@@ -79,6 +80,16 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+
+    if args.only == "copy":
+        nbytes = 1 << 30
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "launches": args.steps}))
+        return
 
     M, din, dout, r, alpha = 2048, 4096, 4096, 64, 16.0
     s = alpha / r

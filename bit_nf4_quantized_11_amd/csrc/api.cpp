@@ -118,15 +118,16 @@ qlora_status check_linear(int64_t M, const qlora_nf4* w, int32_t r) {
   if (w->cols % 64 != 0 || w->rows % 8 != 0) return QLORA_ERR_SHAPE;
   if (w->rows > (int64_t(1) << 22) || w->cols > (int64_t(1) << 22)) return QLORA_ERR_SHAPE;
   if (r < 8 || r > 256 || r % 8 != 0) return QLORA_ERR_UNSUPPORTED;
+  // the large-M kernels address each operand with 32-bit byte offsets
+  const uint64_t lim = uint64_t(1) << 32;
+  const uint64_t in = (uint64_t)w->cols, out = (uint64_t)w->rows;
+  if (((uint64_t)M + 512) * std::max(in, out) * 2 >= lim) return QLORA_ERR_SHAPE;
+  if ((out + 128) * (in / 64) * 32 >= lim) return QLORA_ERR_SHAPE;
   return QLORA_OK;
 }
 
 // ---- workspace layouts ----------------------------------------------------------------------
-struct FwdWs {
-  uint16_t* Ts;
-  float* partial;
-  size_t bytes;
-};
+constexpr int kMaxSplits = 16;
 
 SmallGemm gemm_T(const uint16_t* X, const uint16_t* A, int64_t M, int64_t in, int64_t r) {
   // T[m][j] = sum_k X[m][k] A[k][j]
@@ -147,15 +148,27 @@ SmallGemm gemm_dB(const uint16_t* T, int64_t ldT, const uint16_t* dY, int64_t M,
 
 bool use_gemv(int64_t M) { return M <= 16; }
 
+LoraEpi epi_none() { return LoraEpi{nullptr, 0, 0.0f, nullptr, 0, 0.0f, nullptr, 0.0f}; }
+
+struct FwdWs {
+  uint16_t* Ts;
+  float* partial;
+  LoraProblem t;
+  GemvPlan gv;
+  size_t bytes;
+};
+
 FwdWs fwd_layout(void* base, int64_t M, int64_t in, int64_t out, int32_t r) {
   Carve c(base);
   const int64_t rp = rank_pad(r);
+  const int64_t Mm = std::max<int64_t>(M, 1);
   FwdWs ws;
-  ws.Ts = c.take<uint16_t>((size_t)std::max<int64_t>(M, 1) * rp);
-  const SmallGemm gt = gemm_T(nullptr, nullptr, std::max<int64_t>(M, 1), in, r);
-  size_t pf = small_gemm_partial_floats(gt);
-  if (use_gemv(M)) pf = std::max(pf, (size_t)gemv_splits(in, out) * (size_t)std::max<int64_t>(M, 1) * out);
-  ws.partial = c.take<float>(pf);
+  ws.t = lora_problem(gemm_T(nullptr, nullptr, Mm, in, r), epi_none(), kMaxSplits);
+  ws.gv = gemv_plan(in, out);
+  size_t pf = lora_partial_floats(ws.t);
+  if (use_gemv(M)) pf = std::max(pf, gemv_partial_floats(ws.gv, Mm));
+  ws.Ts = c.take<uint16_t>((size_t)Mm * rp);
+  ws.partial = c.take<float>(std::max<size_t>(pf, 1));
   ws.bytes = round_up(c.off, 256);
   return ws;
 }
@@ -164,6 +177,7 @@ struct BwdWs {
   uint16_t* Gs;
   uint16_t* T;
   float* partial;
+  LoraProblem t, g, da, db;
   size_t bytes;
 };
 
@@ -172,13 +186,15 @@ BwdWs bwd_layout(void* base, int64_t M, int64_t in, int64_t out, int32_t r) {
   const int64_t rp = rank_pad(r);
   const int64_t Mm = std::max<int64_t>(M, 1);
   BwdWs ws;
+  ws.t = lora_problem(gemm_T(nullptr, nullptr, Mm, in, r), epi_none(), kMaxSplits);
+  ws.g = lora_problem(gemm_G(nullptr, nullptr, Mm, out, r), epi_none(), kMaxSplits);
+  ws.da = lora_problem(gemm_dA(nullptr, nullptr, Mm, in, r, rp), epi_none(), kMaxSplits);
+  ws.db = lora_problem(gemm_dB(nullptr, r, nullptr, Mm, out, r), epi_none(), kMaxSplits);
+  const size_t pf = std::max({lora_partial_floats(ws.t), lora_partial_floats(ws.g),
+                              lora_partial_floats(ws.da) + lora_partial_floats(ws.db)});
   ws.Gs = c.take<uint16_t>((size_t)Mm * rp);
   ws.T = c.take<uint16_t>((size_t)Mm * r);
-  size_t pf = small_gemm_partial_floats(gemm_T(nullptr, nullptr, Mm, in, r));
-  pf = std::max(pf, small_gemm_partial_floats(gemm_G(nullptr, nullptr, Mm, out, r)));
-  pf = std::max(pf, small_gemm_partial_floats(gemm_dA(nullptr, nullptr, Mm, in, r, rp)));
-  pf = std::max(pf, small_gemm_partial_floats(gemm_dB(nullptr, r, nullptr, Mm, out, r)));
-  ws.partial = c.take<float>(pf);
+  ws.partial = c.take<float>(std::max<size_t>(pf, 1));
   ws.bytes = round_up(c.off, 256);
   return ws;
 }
@@ -192,7 +208,7 @@ struct QuantWs {
 QuantWs quant_layout(void* base, int64_t numel) {
   Carve c(base);
   QuantWs ws;
-  ws.hist = c.take<unsigned long long>(256);
+  ws.hist = c.take<unsigned long long>(256 * kHistCopies);
   ws.absmax = c.take<float>((size_t)((numel + 63) / 64));
   ws.bytes = round_up(c.off, 256);
   return ws;
@@ -267,7 +283,7 @@ qlora_status qlora_quantize_nf4(const uint16_t* W, int64_t rows, int64_t cols, c
     if (!ws || ws_bytes < need.bytes) return QLORA_ERR_WORKSPACE;
     if (!aligned16(ws)) return QLORA_ERR_ALIGN;
     const QuantWs q = quant_layout(ws, numel);
-    QL_HIP(launch_fill_u32(reinterpret_cast<uint32_t*>(q.hist), 512, 0u, stream));
+    QL_HIP(launch_fill_u32(reinterpret_cast<uint32_t*>(q.hist), 512 * kHistCopies, 0u, stream));
     QL_HIP(launch_quantize(W, numel, out->codes, q.absmax, q.hist, stream));
     QL_HIP(launch_dq_mean(q.hist, nblk, out->mu, stream));
     QL_HIP(launch_dq_encode(q.absmax, nblk, out->mu, static_cast<uint8_t*>(out->absmax), out->c1, stream));
@@ -304,16 +320,15 @@ qlora_status qlora_linear_fwd(const uint16_t* X, int64_t M, const qlora_nf4* w, 
   const FwdWs L = fwd_layout(ws, M, in, out, r);
   const NF4View v = view_of(w);
 
-  // T = X A, split over the reduction; Ts = bf16(s T) padded to rp columns; T_save = bf16(T)
-  const SmallGemm gt = gemm_T(X, A, M, in, r);
-  const int st_splits = small_gemm_splits(gt);
-  QL_HIP(launch_small_gemm(gt, L.partial, st_splits, "k_lora_xa", stream));
-  QL_HIP(launch_small_reduce(L.partial, st_splits, M, r, T_save, r, 1.0f, L.Ts, rp, scale, nullptr, 0.0f,
-                             "k_lora_xa_reduce", stream));
+  // T = X A (bf16 to T_save) and Ts = bf16(s T) padded to rp columns, then the fused product
+  LoraProblem pt = lora_problem(gemm_T(X, A, M, in, r), LoraEpi{T_save, r, 1.0f, L.Ts, rp, scale, nullptr, 0.0f},
+                                kMaxSplits);
+  pt.partial = L.partial;
+  QL_HIP(launch_lora(pt, nullptr, "k_lora_xa", stream));
+  if (pt.splits > 1) QL_HIP(launch_lora_reduce(pt, nullptr, "k_lora_xa_reduce", stream));
   if (use_gemv(M)) {
-    const int sp = gemv_splits(in, out);
-    QL_HIP(launch_gemv(X, M, in, out, v, L.partial, sp, stream));
-    QL_HIP(launch_gemv_epilogue(L.partial, sp, M, out, L.Ts, rp, B, r, Y, stream));
+    QL_HIP(launch_gemv(X, M, in, out, v, L.gv, L.partial, stream));
+    QL_HIP(launch_gemv_epilogue(L.partial, L.gv, M, out, L.Ts, rp, B, r, Y, stream));
   } else {
     QL_HIP(launch_fwd_gemm(X, M, in, out, v, L.Ts, rp, B, r, Y, stream));
   }
@@ -343,32 +358,35 @@ qlora_status qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, const uint1
 
   const uint16_t* T = T_saved;
   if (!T) {
-    const SmallGemm gt = gemm_T(X, A, M, in, r);
-    const int sp = small_gemm_splits(gt);
-    QL_HIP(launch_small_gemm(gt, L.partial, sp, "k_lora_xa", stream));
-    QL_HIP(launch_small_reduce(L.partial, sp, M, r, L.T, r, 1.0f, nullptr, 0, 0.0f, nullptr, 0.0f,
-                               "k_lora_xa_reduce", stream));
+    LoraProblem pt = lora_problem(gemm_T(X, A, M, in, r), LoraEpi{L.T, r, 1.0f, nullptr, 0, 0.0f, nullptr, 0.0f},
+                                  kMaxSplits);
+    pt.partial = L.partial;
+    QL_HIP(launch_lora(pt, nullptr, "k_lora_xa", stream));
+    if (pt.splits > 1) QL_HIP(launch_lora_reduce(pt, nullptr, "k_lora_xa_reduce", stream));
     T = L.T;
   }
   // Gs = bf16(s dY B^T), padded to rp columns
-  const SmallGemm gg = gemm_G(dY, B, M, out, r);
-  const int sg = small_gemm_splits(gg);
-  QL_HIP(launch_small_gemm(gg, L.partial, sg, "k_lora_dyb", stream));
-  QL_HIP(launch_small_reduce(L.partial, sg, M, r, nullptr, 0, 0.0f, L.Gs, rp, scale, nullptr, 0.0f,
-                             "k_lora_dyb_reduce", stream));
+  LoraProblem pg = lora_problem(gemm_G(dY, B, M, out, r), LoraEpi{nullptr, 0, 0.0f, L.Gs, rp, scale, nullptr, 0.0f},
+                                kMaxSplits);
+  pg.partial = L.partial;
+  QL_HIP(launch_lora(pg, nullptr, "k_lora_dyb", stream));
+  if (pg.splits > 1) QL_HIP(launch_lora_reduce(pg, nullptr, "k_lora_dyb_reduce", stream));
   if (dX) QL_HIP(launch_dx_gemm(dY, M, in, out, v, L.Gs, rp, A, r, dX, stream));
-  // dA = X^T Gs
-  const SmallGemm ga = gemm_dA(X, L.Gs, M, in, r, rp);
-  const int sa = small_gemm_splits(ga);
-  QL_HIP(launch_small_gemm(ga, L.partial, sa, "k_lora_da", stream));
-  QL_HIP(launch_small_reduce(L.partial, sa, in, r, nullptr, 0, 0.0f, nullptr, 0, 0.0f, dA, 1.0f, "k_lora_da_reduce",
-                             stream));
-  // dB = s T^T dY
-  const SmallGemm gb = gemm_dB(T, r, dY, M, out, r);
-  const int sb = small_gemm_splits(gb);
-  QL_HIP(launch_small_gemm(gb, L.partial, sb, "k_lora_db", stream));
-  QL_HIP(launch_small_reduce(L.partial, sb, r, out, nullptr, 0, 0.0f, nullptr, 0, 0.0f, dB, scale, "k_lora_db_reduce",
-                             stream));
+  // dA = X^T Gs and dB = s T^T dY, one launch for both products and one for both reductions
+  LoraProblem pa = lora_problem(gemm_dA(X, L.Gs, M, in, r, rp),
+                                LoraEpi{nullptr, 0, 0.0f, nullptr, 0, 0.0f, dA, 1.0f}, kMaxSplits);
+  LoraProblem pb = lora_problem(gemm_dB(T, r, dY, M, out, r),
+                                LoraEpi{nullptr, 0, 0.0f, nullptr, 0, 0.0f, dB, scale}, kMaxSplits);
+  pa.partial = L.partial;
+  pb.partial = L.partial + lora_partial_floats(pa);
+  QL_HIP(launch_lora(pa, &pb, "k_lora_da_db", stream));
+  if (pa.splits > 1 || pb.splits > 1) {
+    // a product computed in one split wrote its outputs directly; reduce only the others
+    if (pa.splits > 1 && pb.splits > 1)
+      QL_HIP(launch_lora_reduce(pa, &pb, "k_lora_da_db_reduce", stream));
+    else
+      QL_HIP(launch_lora_reduce(pa.splits > 1 ? pa : pb, nullptr, "k_lora_da_db_reduce", stream));
+  }
   return QLORA_OK;
 }
 

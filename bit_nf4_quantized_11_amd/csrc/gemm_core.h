@@ -5,9 +5,16 @@
 // reducing over 64 at a time through a double-buffered LDS stage:
 //   sT  [256][64]  token operand (X or dY, or the adapter activations), bf16
 //   sF  [128][64]  feature operand (dequantized weight, or the adapter factor), bf16
-// Rows of both are 64 bf16 = eight 16-byte chunks; chunk c of row r is stored at
-// chunk position c ^ (r & 7), so the 16 rows read by one MFMA fragment fall in
-// distinct banks.
+// Each tile is stored as two halves (reduction 0..31 and 32..63), each half as rows
+// of four 16-byte chunks (64 bytes).  Chunk c of row r sits at position
+// c ^ ((r >> 1) & 3): eight consecutive rows then cover all 32 banks for any chunk,
+// which is what one MFMA fragment read touches per cycle, and the second half and
+// the second buffer are constant offsets (immediate fields of the LDS instructions).
+//
+// Global loads go through raw buffer resources: an access past the end of a
+// buffer returns zero, so tile edges need no branches.  Stage s is loaded into
+// registers two stages ahead, and its LDS store is cut into eight pieces that
+// sit between the eight groups of MFMAs of the stage being computed.
 //
 // The MFMA computes C[feature][token]: operand A = feature rows, operand B =
 // token rows.  Lane l of a 16x16 result holds C[4*(l/16) + v][l % 16], v = 0..3,
@@ -25,32 +32,41 @@ constexpr int BF = 128;   // features per tile
 constexpr int BR = 64;    // reduction per stage
 constexpr int NT = 256;   // threads
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * BR + ((chunk ^ (row & 7)) << 3); }
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
-// Token operand stage: rows m0..m0+255, reduction columns c0..c0+63 of a row-major
-// [rows][ld] bf16 matrix; rows >= nrows and columns >= ncols read as zero
-// (ncols % 8 == 0).  Thread t loads chunk t%8 of rows t/8 + 32 i.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint64_t bytes) {
+  // raw buffer, 32-bit data format word for gfx9-family buffer instructions
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)(uint32_t)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 ld16(rsrc_t r, uint32_t byte_off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// element offset of 16-byte chunk `chunk` (0..7) of row `row` in a tile of `rows` rows
+__device__ __forceinline__ int swz_t(int rows, int row, int chunk) {
+  return (chunk >> 2) * rows * 32 + row * 32 + (((chunk & 3) ^ ((row >> 1) & 3)) << 3);
+}
+__device__ __forceinline__ int swzT(int row, int chunk) { return swz_t(BT, row, chunk); }
+__device__ __forceinline__ int swzF(int row, int chunk) { return swz_t(BF, row, chunk); }
+
+// Token operand: rows m0..m0+255, columns c0..c0+63 of a row-major [rows][ld] bf16
+// matrix.  Thread t holds chunk t%8 of rows t/8 + 32 i.
 struct TokenRegs {
   uint4 v[8];
 };
 
-__device__ __forceinline__ void load_tokens(TokenRegs& R, const uint16_t* __restrict__ P, int64_t ld, int64_t m0,
-                                            int64_t nrows, int64_t c0, int64_t ncols) {
+__device__ __forceinline__ void load_tokens(TokenRegs& R, rsrc_t src, uint32_t ld, uint32_t m0, uint32_t c0) {
   const int t = threadIdx.x;
-  const int c = t & 7;
-  const int64_t col = c0 + c * 8;
+  const uint32_t base = ((m0 + (t >> 3)) * ld + c0 + (t & 7) * 8) * 2;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t row = m0 + (t >> 3) + 32 * i;
-    R.v[i] = make_uint4(0, 0, 0, 0);
-    if (row < nrows && col < ncols) R.v[i] = *reinterpret_cast<const uint4*>(P + row * ld + col);
-  }
+  for (int i = 0; i < 8; ++i) R.v[i] = ld16(src, base + (uint32_t)(32 * i) * ld * 2);
 }
 
-__device__ __forceinline__ void store_tokens(const TokenRegs& R, uint16_t* __restrict__ sT) {
+__device__ __forceinline__ void store_tokens_part(const TokenRegs& R, uint16_t* __restrict__ sT, int i) {
   const int t = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(sT + swz((t >> 3) + 32 * i, t & 7)) = R.v[i];
+  *reinterpret_cast<uint4*>(sT + swzT((t >> 3) + 32 * i, t & 7)) = R.v[i];
 }
 
 struct Acc {
@@ -64,24 +80,37 @@ __device__ __forceinline__ void acc_zero(Acc& a) {
     for (int m = 0; m < 8; ++m) a.c[f][m] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
-// One 64-deep stage: wave (wt, wf) covers tokens wt*128.., features wf*64..
-__device__ __forceinline__ void mma_stage(Acc& a, const uint16_t* __restrict__ sT, const uint16_t* __restrict__ sF) {
+struct Frags {
+  u32x4 fa[4], tb[8];
+};
+
+// wave (wt, wf) covers tokens wt*128.., features wf*64..; ks selects 32 of the 64
+__device__ __forceinline__ void read_frags(Frags& F, const uint16_t* __restrict__ sT,
+                                           const uint16_t* __restrict__ sF, int ks) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wt = wave & 1, wf = wave >> 1;
+  const int chunk = ks * 4 + (lane >> 4);
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+    F.fa[f] = *reinterpret_cast<const u32x4*>(sF + swzF(wf * 64 + f * 16 + (lane & 15), chunk));
+#pragma unroll
+  for (int m = 0; m < 8; ++m)
+    F.tb[m] = *reinterpret_cast<const u32x4*>(sT + swzT(wt * 128 + m * 16 + (lane & 15), chunk));
+}
+
+__device__ __forceinline__ void mma_group(Acc& a, const Frags& F, int f) {
+#pragma unroll
+  for (int m = 0; m < 8; ++m) a.c[f][m] = mfma16(F.fa[f], F.tb[m], a.c[f][m]);
+}
+
+// One 64-deep stage without interleaved work (tail stages).
+__device__ __forceinline__ void mma_stage(Acc& a, const uint16_t* __restrict__ sT, const uint16_t* __restrict__ sF) {
+  Frags F;
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
-    const int chunk = ks * 4 + (lane >> 4);
-    u32x4 fa[4], tb[8];
+    read_frags(F, sT, sF, ks);
 #pragma unroll
-    for (int f = 0; f < 4; ++f)
-      fa[f] = *reinterpret_cast<const u32x4*>(sF + swz(wf * 64 + f * 16 + (lane & 15), chunk));
-#pragma unroll
-    for (int m = 0; m < 8; ++m)
-      tb[m] = *reinterpret_cast<const u32x4*>(sT + swz(wt * 128 + m * 16 + (lane & 15), chunk));
-#pragma unroll
-    for (int f = 0; f < 4; ++f)
-#pragma unroll
-      for (int m = 0; m < 8; ++m) a.c[f][m] = mfma16(fa[f], tb[m], a.c[f][m]);
+    for (int f = 0; f < 4; ++f) mma_group(a, F, f);
   }
 }
 

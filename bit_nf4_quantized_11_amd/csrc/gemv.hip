@@ -9,8 +9,8 @@
 // (v_mfma_f32_16x16x32_bf16) takes 8 weights from each of 4 blocks; 8 MFMAs
 // consume the 4 blocks.  The MFMA's reduction index is therefore a permutation of
 // k, applied identically to the token operand read from LDS (tokens beyond M are
-// zero).  Result C[n][m] per wave; split-K partial sums go to fp32 scratch, and a
-// second kernel adds the splits in a fixed order, adds the adapter term
+// zero).  Result C[n][m] per wave; each split writes its fp32 partial sums, and an
+// epilogue kernel adds the splits in split order, adds the adapter term
 // Ts[M][rp] B and rounds to bf16 once.
 #include "common.h"
 #include "kernels.h"
@@ -27,8 +27,9 @@ struct GemvParams {
   const uint16_t* X;
   int64_t M, K, N;
   NF4View w;
-  float* partial;   // [splits][M][N]
+  float* partial;       // [groups][splits][M][64]
   int64_t kb_per_split;
+  int splits;
   NF4Table tab;
 };
 
@@ -38,8 +39,9 @@ __device__ __forceinline__ int xsw(int m, int c) { return (c ^ (m & 7)); }
 __global__ __launch_bounds__(GT) void k_fwd_nf4_gemv(GemvParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t sX[16 * GMAX_KS];
   const int64_t nkb = p.K / 64;
-  const int64_t n0 = (int64_t)blockIdx.x * GROWS;
-  const int split = blockIdx.y;
+  const int64_t grp_id = (int64_t)blockIdx.x / p.splits;
+  const int split = (int)((int64_t)blockIdx.x - grp_id * p.splits);
+  const int64_t n0 = grp_id * GROWS;
   const int64_t kb_beg = split * p.kb_per_split;
   const int64_t kb_end = min(nkb, kb_beg + p.kb_per_split);
   const int64_t nkb_s = kb_end - kb_beg;
@@ -87,70 +89,69 @@ __global__ __launch_bounds__(GT) void k_fwd_nf4_gemv(GemvParams p) {
       acc = mfma16(wa, xb, acc);
     }
   }
-  // acc[v] = C[n = n0 + wave*16 + 4*grp + v][m = row]
+  // acc[v] = C[n = n0 + wave*16 + 4*grp + v][m = row]; this split's partial tile is [M][64]
+  float* part = p.partial + (grp_id * p.splits + split) * p.M * GROWS;
   if (tok_ok) {
-    const int64_t nn = n0 + wave * 16 + 4 * grp;
-    if (nn < p.N) {
-      float4 o = make_float4(acc[0], acc[1], acc[2], acc[3]);
-      *reinterpret_cast<float4*>(p.partial + ((int64_t)split * p.M + row) * p.N + nn) = o;
-    }
+    const float4 o = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    *reinterpret_cast<float4*>(part + row * GROWS + wave * 16 + 4 * grp) = o;
   }
 }
 
+// Y[m][n] = bf16( sum over splits (in order) + sum_j Ts[m][j] B[j][n] ); one thread per output
 __global__ __launch_bounds__(256) void k_gemv_epilogue(const float* __restrict__ partial, int splits, int64_t M,
                                                        int64_t N, const uint16_t* __restrict__ Ts, int64_t rp,
                                                        const uint16_t* __restrict__ B, int64_t r,
                                                        uint16_t* __restrict__ Y) {
-  const int64_t total = M * N;
-  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
-       idx += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t m = idx / N, n = idx - m * N;
-    float sum = 0.0f;
-    for (int s = 0; s < splits; ++s) sum = __fadd_rn(sum, partial[((int64_t)s * M + m) * N + n]);
-    float lora = 0.0f;
-    for (int64_t j = 0; j < r; ++j) lora = __builtin_fmaf(bf16_to_f32(Ts[m * rp + j]), bf16_to_f32(B[j * N + n]), lora);
-    Y[idx] = (uint16_t)f32_to_bf16_bits(__fadd_rn(sum, lora));
-  }
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;   // over [groups][M][64]
+  const int64_t per_group = M * GROWS;
+  const int64_t grp_id = idx / per_group;
+  const int e = (int)(idx - grp_id * per_group);
+  const int m = e / GROWS, nl = e - m * GROWS;
+  const int64_t n = grp_id * GROWS + nl;
+  if (n >= N) return;
+  const float* base = partial + grp_id * splits * per_group + e;
+  float sum = 0.0f;
+  for (int sp = 0; sp < splits; ++sp) sum = __fadd_rn(sum, base[sp * per_group]);
+  float lora = 0.0f;
+  for (int64_t j = 0; j < r; ++j) lora = __builtin_fmaf(bf16_to_f32(Ts[m * rp + j]), bf16_to_f32(B[j * N + n]), lora);
+  Y[m * N + n] = (uint16_t)f32_to_bf16_bits(__fadd_rn(sum, lora));
 }
 
 }  // namespace
 
-// Blocks of the reduction per split: whole 4-block steps, at most GMAX_KS columns,
-// and enough splits for about 1024 workgroups.
-static int64_t gemv_kb_per_split(int64_t K, int64_t N) {
+// Blocks of the reduction per split: whole 4-block steps, at most GMAX_KS columns
+// (the LDS token tile), and enough splits for about 1024 workgroups.
+GemvPlan gemv_plan(int64_t K, int64_t N) {
   const int64_t nkb = K / 64;
-  const int64_t groups = (N + GROWS - 1) / GROWS;
-  int64_t s = (1024 + groups - 1) / groups;
+  GemvPlan pl;
+  pl.groups = (N + GROWS - 1) / GROWS;
+  int64_t s = (1024 + pl.groups - 1) / pl.groups;
   if (s > nkb) s = nkb;
   if (s < 1) s = 1;
   int64_t kbps = (nkb + s - 1) / s;
   kbps = (kbps + 3) / 4 * 4;
   if (kbps * 64 > GMAX_KS) kbps = GMAX_KS / 64;
-  return kbps;
+  pl.kb_per_split = kbps;
+  pl.splits = (int)((nkb + kbps - 1) / kbps);
+  return pl;
 }
 
-int gemv_splits(int64_t K, int64_t N) {
-  const int64_t kbps = gemv_kb_per_split(K, N);
-  return (int)((K / 64 + kbps - 1) / kbps);
-}
+size_t gemv_partial_floats(const GemvPlan& pl, int64_t M) { return (size_t)(pl.groups * pl.splits * M * GROWS); }
 
-hipError_t launch_gemv(const uint16_t* X, int64_t M, int64_t K, int64_t N, const NF4View& w, float* partial,
-                       int splits, hipStream_t s) {
-  const int64_t kbps = gemv_kb_per_split(K, N);
-  GemvParams p{X, M, K, N, w, partial, kbps, nf4_table()};
-  dim3 grid((unsigned)((N + GROWS - 1) / GROWS), (unsigned)splits);
+hipError_t launch_gemv(const uint16_t* X, int64_t M, int64_t K, int64_t N, const NF4View& w, const GemvPlan& pl,
+                       float* partial, hipStream_t s) {
+  GemvParams p{X, M, K, N, w, partial, pl.kb_per_split, pl.splits, nf4_table()};
   ProfScope ps("k_fwd_nf4_gemv", s);
-  hipLaunchKernelGGL(k_fwd_nf4_gemv, grid, dim3(GT), 0, s, p);
+  hipLaunchKernelGGL(k_fwd_nf4_gemv, dim3((unsigned)(pl.groups * pl.splits)), dim3(GT), 0, s, p);
   return hipGetLastError();
 }
 
-hipError_t launch_gemv_epilogue(const float* partial, int splits, int64_t M, int64_t N, const uint16_t* Ts,
+hipError_t launch_gemv_epilogue(const float* partial, const GemvPlan& pl, int64_t M, int64_t N, const uint16_t* Ts,
                                 int64_t rp, const uint16_t* B, int64_t r, uint16_t* Y, hipStream_t s) {
-  int64_t grid = (M * N + 255) / 256;
-  if (grid > 8192) grid = 8192;
-  if (grid < 1) grid = 1;
+  const int64_t n = pl.groups * M * GROWS;
   ProfScope ps("k_gemv_epilogue", s);
-  hipLaunchKernelGGL(k_gemv_epilogue, dim3((unsigned)grid), dim3(256), 0, s, partial, splits, M, N, Ts, rp, B, r, Y);
+  hipLaunchKernelGGL(k_gemv_epilogue, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, partial, pl.splits, M, N,
+                     Ts, rp, B, r, Y);
   return hipGetLastError();
 }
 

@@ -33,8 +33,8 @@ hipError_t launch_dq_encode(const float* absmax_f32, int64_t nblk, const float* 
 hipError_t launch_dequant(const NF4View& w, int64_t numel, uint16_t* out, hipStream_t s);
 
 // ---- small rank-r products (lora.hip) ----------------------------------------------------
-// partial[split][I][J] = sum_{k in split} A(i,k) B(k,j); A(i,k) = A[i*a_si + k*a_sk] (one of the two
-// strides is 1), B(k,j) = B[k*b_sk + j*b_sj] (one of the two strides is 1).
+// C[I][J] = sum_k A(i,k) B(k,j); A(i,k) = A[i*a_si + k*a_sk] (one of the two strides is 1),
+// B(k,j) = B[k*b_sk + j*b_sj] (one of the two strides is 1).
 struct SmallGemm {
   const uint16_t* A;
   int64_t a_si, a_sk;
@@ -42,15 +42,33 @@ struct SmallGemm {
   int64_t b_sk, b_sj;
   int64_t I, J, K;
 };
-int small_gemm_splits(const SmallGemm& g);
-size_t small_gemm_partial_floats(const SmallGemm& g);
-hipError_t launch_small_gemm(const SmallGemm& g, float* partial, int splits, const char* name, hipStream_t s);
-// out_a[i*lda + j] = bf16(scale_a * sum)   (j < J; NULL to skip)
-// out_b[i*ldb + j] = bf16(scale_b * sum)   (j < J), 0 for J <= j < ldb  (NULL to skip)
-// out_f[i*J + j]   = scale_f * sum         (NULL to skip)
-hipError_t launch_small_reduce(const float* partial, int splits, int64_t I, int64_t J, uint16_t* out_a, int64_t lda,
-                               float scale_a, uint16_t* out_b, int64_t ldb, float scale_b, float* out_f,
-                               float scale_f, const char* name, hipStream_t s);
+// Outputs of a product (any may be NULL):
+//   out_a[i*lda + j] = bf16(scale_a * C)                     (j < J)
+//   out_b[i*ldb + j] = bf16(scale_b * C) for j < J, 0 for J <= j < ldb
+//   out_f[i*J + j]   = scale_f * C
+struct LoraEpi {
+  uint16_t* out_a;
+  int64_t lda;
+  float scale_a;
+  uint16_t* out_b;
+  int64_t ldb;
+  float scale_b;
+  float* out_f;
+  float scale_f;
+};
+struct LoraProblem {
+  SmallGemm g;
+  LoraEpi ep;
+  int64_t tiles_i, tiles_j, k_per_split;
+  int splits;
+  float* partial;        // splits > 1: tiles * splits * 64*64 floats of workspace
+};
+LoraProblem lora_problem(const SmallGemm& g, const LoraEpi& ep, int max_splits);
+size_t lora_partial_floats(const LoraProblem& p);
+// one launch for p0, or for p0 and p1 together (same operand layouts); with splits > 1
+// the partials are summed and written out by launch_lora_reduce
+hipError_t launch_lora(const LoraProblem& p0, const LoraProblem* p1, const char* name, hipStream_t s);
+hipError_t launch_lora_reduce(const LoraProblem& p0, const LoraProblem* p1, const char* name, hipStream_t s);
 
 // ---- fused forward, large M (fwd_gemm.hip) ------------------------------------------------
 // Y[M][N] = bf16( X[M][K] deq(W)^T + Ts[M][rp] Bt ), Bt(j, n) = B[j][n] for j < r else 0.
@@ -59,10 +77,19 @@ hipError_t launch_fwd_gemm(const uint16_t* X, int64_t M, int64_t K, int64_t N, c
                            hipStream_t s);
 
 // ---- fused forward, skinny M <= 16 (gemv.hip) ---------------------------------------------
-int gemv_splits(int64_t K, int64_t N);
-hipError_t launch_gemv(const uint16_t* X, int64_t M, int64_t K, int64_t N, const NF4View& w, float* partial,
-                       int splits, hipStream_t s);
-hipError_t launch_gemv_epilogue(const float* partial, int splits, int64_t M, int64_t N, const uint16_t* Ts,
+// Y[M][N] = bf16( X deq(W)^T + Ts[M][rp] B ): the dequantizing product split over the
+// reduction into fp32 partials, then an epilogue kernel that adds the splits in
+// order and the adapter term.
+struct GemvPlan {
+  int splits;
+  int64_t kb_per_split;
+  int64_t groups;
+};
+GemvPlan gemv_plan(int64_t K, int64_t N);
+size_t gemv_partial_floats(const GemvPlan& pl, int64_t M);
+hipError_t launch_gemv(const uint16_t* X, int64_t M, int64_t K, int64_t N, const NF4View& w, const GemvPlan& pl,
+                       float* partial, hipStream_t s);
+hipError_t launch_gemv_epilogue(const float* partial, const GemvPlan& pl, int64_t M, int64_t N, const uint16_t* Ts,
                                 int64_t rp, const uint16_t* B, int64_t r, uint16_t* Y, hipStream_t s);
 
 // ---- backward dX (dx_gemm.hip) --------------------------------------------------------------

@@ -79,9 +79,11 @@ __global__ __launch_bounds__(kThreads) void k_nf4_quantize(const uint16_t* __res
     }
   }
   if (dq) {
+    // one of kHistCopies global copies per workgroup, so the few busy bins do not
+    // serialize every workgroup's atomics on one address
     __syncthreads();
     const unsigned long long v = lhist[threadIdx.x];
-    if (v) atomicAdd(&hist[threadIdx.x], v);
+    if (v) atomicAdd(&hist[(blockIdx.x % kHistCopies) * 256 + threadIdx.x], v);
   }
 }
 
@@ -89,15 +91,30 @@ __global__ __launch_bounds__(kThreads) void k_nf4_quantize(const uint16_t* __res
 // hist[E] = sum of the 8-bit significands (implicit bit included) of the constants whose
 // bf16 exponent field is E, so S = sum_E hist[E] * 2^(E - 134).  The exact integer
 // sum_E hist[E] << E is built in 64-bit words, then rounded to nearest even.
-__global__ void k_dq_mean(const unsigned long long* __restrict__ hist, int64_t nblk, float* __restrict__ mu) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+__global__ __launch_bounds__(256) void k_dq_mean(const unsigned long long* __restrict__ hist, int64_t nblk,
+                                                 float* __restrict__ mu) {
+  __shared__ unsigned long long tot[256];
+  __shared__ unsigned long long nonzero[4];
+  {
+    unsigned long long v = 0;
+#pragma unroll 16
+    for (int c = 0; c < kHistCopies; ++c) v += hist[c * 256 + threadIdx.x];
+    tot[threadIdx.x] = v;
+    const unsigned long long b = __ballot(v != 0ull);
+    if ((threadIdx.x & 63) == 0) nonzero[threadIdx.x >> 6] = b;
+  }
+  __syncthreads();
+  if (threadIdx.x != 0) return;
   constexpr int NW = 7;   // 448 bits: 2^254 * 2^64 fits
   unsigned long long acc[NW];
 #pragma unroll
   for (int k = 0; k < NW; ++k) acc[k] = 0ull;
-  for (int E = 1; E < 255; ++E) {
-    const unsigned long long v = hist[E];
-    if (!v) continue;
+  // only the occupied exponent bins, in increasing order (bin 0 only ever holds zeros)
+  for (int wv = 0; wv < 4; ++wv)
+  for (unsigned long long bits = nonzero[wv]; bits; bits &= bits - 1ull) {
+    const int E = wv * 64 + __builtin_ctzll(bits);
+    if (E == 0 || E == 255) continue;
+    const unsigned long long v = tot[E];
     const int w = E >> 6, sh = E & 63;
     const unsigned long long lo = v << sh;
     const unsigned long long hi = sh ? (v >> (64 - sh)) : 0ull;
@@ -233,14 +250,14 @@ hipError_t launch_quantize(const uint16_t* W, int64_t numel, uint8_t* codes, flo
                            unsigned long long* hist, hipStream_t s) {
   const int64_t nblk = (numel + 63) / 64;
   ProfScope ps("k_nf4_quantize", s);
-  hipLaunchKernelGGL(k_nf4_quantize, dim3(grid_for(nblk, kThreads / 8, 8192)), dim3(kThreads), 0, s, W, numel,
+  hipLaunchKernelGGL(k_nf4_quantize, dim3(grid_for(nblk, kThreads / 8, 2048)), dim3(kThreads), 0, s, W, numel,
                      codes, absmax_f32, hist, nf4_table());
   return hipGetLastError();
 }
 
 hipError_t launch_dq_mean(const unsigned long long* hist, int64_t nblk, float* mu, hipStream_t s) {
   ProfScope ps("k_dq_mean", s);
-  hipLaunchKernelGGL(k_dq_mean, dim3(1), dim3(64), 0, s, hist, nblk, mu);
+  hipLaunchKernelGGL(k_dq_mean, dim3(1), dim3(256), 0, s, hist, nblk, mu);
   return hipGetLastError();
 }
 
