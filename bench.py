@@ -46,6 +46,32 @@ def weight_bytes(din, dout):
     return 32 * nblk + nblk + 4 * (-(-nblk // 256)) + 4
 
 
+KERNEL_SOURCES = {
+    "k_fwd_nf4_gemm": ["fwd_gemm.hip", "gemm_core.h", "common.h"],
+    "k_bwd_dx_nf4_gemm": ["dx_gemm.hip", "gemm_core.h", "common.h"],
+    "k_nf4_quantize": ["quant.hip", "common.h"],
+    "k_fwd_nf4_gemv": ["gemv.hip", "common.h"],
+}
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE runs (scaled by a
+    plain copy's counts), or None if the kernel's sources changed since the counters were taken."""
+    import hashlib
+
+    root = os.path.dirname(os.path.abspath(__file__))
+    try:
+        with open(os.path.join(root, "profiles", "traffic_counters.txt")) as f:
+            rec = json.load(f)["kernels"][kernel]
+        h = hashlib.sha256()
+        for name in KERNEL_SOURCES[kernel]:
+            with open(os.path.join(root, "bit_nf4_quantized_11_amd", "csrc", name), "rb") as f:
+                h.update(f.read())
+    except (OSError, KeyError, ValueError):
+        return None
+    return rec["traffic_bytes"] if h.hexdigest()[:16] == rec["sources_sha256_16"] else None
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -160,8 +186,11 @@ def main():
                 "k_bwd_dx_nf4_gemm": 2 * M * dout * din + 2 * M * r * din}
         dom = max((k for k in kern if k in algo), key=lambda k: kern[k]["us_per_step"])
         ach = algo[dom] / (kern[dom]["avg_us"] * 1e-6) / 1e12
+        algo_bytes = 2 * M * din + 2 * M * dout + weight_bytes(din, dout) + 2 * r * (din + dout) + 2 * M * 64
         result["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
-                              "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS, "traffic": None,
+                              "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS, "traffic": measured_traffic(dom),
+                              "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)",
+                              "algorithmic_bytes": algo_bytes,
                               "flops_per_launch": algo[dom], "avg_us": kern[dom]["avg_us"]}
         fb_us = sum(v["us_per_step"] for k, v in kern.items() if k not in ("k_nf4_quantize", "k_dq_mean",
                                                                               "k_dq_encode", "k_fill_u32"))
