@@ -55,9 +55,11 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 // Two fp32 -> {bf16(lo), bf16(hi)} with round to nearest even.  On gfx950 this is
 // one v_cvt_pk_bf16_f32, which was checked against the integer rounding above on
 // every non-NaN fp32 bit pattern (denormals and ties included) with no mismatch.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(unsigned short, a) | ((uint32_t)__builtin_bit_cast(unsigned short, b) << 16);
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // ------------------------------------------------------------------------------------------

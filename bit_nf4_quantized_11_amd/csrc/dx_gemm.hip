@@ -5,9 +5,10 @@
 //   dX[M][K] = bf16( dY[M][N] deq(W) + Gs[M][rp] A~^T ),  A~(k, j) = A[k][j] (j < r), 0 otherwise
 //
 // with Gs = bf16(s * dY B^T) from the rank-r kernel.  The reduction runs over the
-// weight's rows n, while each stored row is contiguous along k, so the
-// dequantized tile is written transposed into the feature-major LDS tile
-// sF[k][n] (2-byte stores).  The adapter stages need no transpose: A is [K][r].
+// weight's rows n while each stored row is contiguous along k, so a stage (64 weight
+// rows x 128 columns) is dequantized into the natural LDS tile as stored and the
+// MFMA operand is gathered with transposing LDS reads.  The adapter stages use the
+// feature-major tile: A is [K][r].
 #include "common.h"
 #include "gemm_core.h"
 #include "kernels.h"
@@ -32,10 +33,9 @@ struct DxParams {
 };
 
 struct WRegs {
-  uint4 code;     // 32 codes: half of block (n, kb)
+  uint2 code;     // 16 codes: a quarter of block (n, kb)
   uint32_t c2;
   float c1;
-  uint32_t live;  // the weight row exists (n < N)
 };
 
 struct Stage {
@@ -43,10 +43,12 @@ struct Stage {
   WRegs W;
 };
 
-template <bool DQ>
+// RAGGED: N % 64 != 0, the last stage's token columns past N are masked to zero
+template <bool DQ, bool RAGGED>
 __global__ __launch_bounds__(NT) void k_bwd_dx_nf4_gemm(DxParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t sT[2][BT * BR];
-  __shared__ __attribute__((aligned(16))) uint16_t sF[2][BF * BR];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM_ELEMS];
+  uint16_t* const sT[2] = {smem, smem + TILE_T};
+  uint16_t* const sF[2] = {smem + 2 * TILE_T, smem + 2 * TILE_T + TILE_F};
 
   int64_t tt, tf;
   tile_of((p.M + BT - 1) / BT, (p.K + BF - 1) / BF, tt, tf);
@@ -55,23 +57,28 @@ __global__ __launch_bounds__(NT) void k_bwd_dx_nf4_gemm(DxParams p) {
   const uint32_t N = (uint32_t)p.N;
   const uint32_t nred = (N + 63) / 64;   // reduction stages over the weight rows
   const int t = threadIdx.x;
-  // NF4 stage mapping: weight row t/4 of the stage, block k0/64 + (t/2)%2, half t%2
-  const int wrow = t >> 2, wbsel = (t >> 1) & 1, whalf = t & 1;
-  const uint32_t wkb = k0 / 64 + wbsel;
-  const int kl0 = wbsel * 64 + whalf * 32;   // first feature row of this thread in sF
+  // NF4 stage mapping: weight row t/8 of the stage, block k0/64 + b (b = (t/4)%2), quarter
+  // q = t%4 (groups 2q, 2q+1 -> chunks 8b+2q, 8b+2q+1 of the natural row).  Rows past N
+  // read as zero codes and scale mu; the token operand is zero there.  Columns past K
+  // belong to outputs that are not stored.
+  const int wrow = t >> 3, wb = (t >> 2) & 1, wq = t & 3;
+  const uint32_t wkb = k0 / 64 + wb;
 
-  const rsrc_t rD = make_rsrc(p.dY, (uint64_t)p.M * p.N * 2);
+  const TokenSrc ds = token_src(p.dY, (uint64_t)p.M * p.N * 2, N, m0);
   const rsrc_t rC = make_rsrc(p.w.codes, p.codes_bytes);
   const rsrc_t rA = make_rsrc(p.w.absmax, p.absmax_bytes);
   const rsrc_t rC1 = make_rsrc(p.w.c1, p.c1_bytes);
   constexpr bool dq = DQ;
   const float mu = dq ? *p.w.mu : 0.0f;
+  const QuadLevels lev = quad_levels(p.tab);
 
   auto load = [&](uint32_t it, Stage& S) {
-    load_tokens(S.T, rD, N, m0, it * 64);
-    const uint32_t n = it * 64 + wrow;
-    const uint32_t blk = n * nkb + wkb;
-    S.W.code = ld16(rC, blk * kBlockBytes + whalf * 16);
+    if constexpr (RAGGED)
+      load_tokens_edge(S.T, ds, it * 64, N);
+    else
+      load_tokens(S.T, ds, it * 64);
+    const uint32_t blk = (it * 64 + wrow) * nkb + wkb;
+    S.W.code = ld8(rC, blk * kBlockBytes + wq * 8);
     if constexpr (dq) {
       S.W.c2 = __builtin_amdgcn_raw_buffer_load_b8(rA, blk, 0, 0);
       S.W.c1 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rC1, (blk >> 8) * 4, 0, 0));
@@ -79,109 +86,87 @@ __global__ __launch_bounds__(NT) void k_bwd_dx_nf4_gemm(DxParams p) {
       S.W.c2 = __builtin_amdgcn_raw_buffer_load_b32(rA, blk * 4, 0, 0);
       S.W.c1 = 0.0f;
     }
-    S.W.live = n < N;
   };
 
-  // rows past the last weight row must contribute exact zeros (the token operand there
-  // holds the next token row's values): code 7 is the exact-zero level, scale 0
   auto scale_of = [&](const Stage& S) -> float {
-    const float s = dq ? __fadd_rn(__fmul_rn(e4m3_decode(S.W.c2), S.W.c1), mu) : __uint_as_float(S.W.c2);
-    return S.W.live ? s : 0.0f;
+    return dq ? __fadd_rn(__fmul_rn(e4m3_decode(S.W.c2), S.W.c1), mu) : __uint_as_float(S.W.c2);
   };
-  auto codes_of = [&](const Stage& S, uint32_t q) -> uint32_t {
-    const uint32_t c = q == 0 ? S.W.code.x : q == 1 ? S.W.code.y : q == 2 ? S.W.code.z : S.W.code.w;
-    return S.W.live ? c : 0x77777777u;
-  };
-  // dequantize 8 weights (k = kl0 + 8q .. +7 of row wrow) and write them transposed
-  auto put8 = [&](const Planes& pl, uint32_t cw, int q, int sb) {
-    const u32x4 v = dequant8(pl, cw);
-    const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int kl = kl0 + q * 8 + e;
-      sF[sb][swzF(kl, wrow >> 3) + (wrow & 7)] = (uint16_t)((e & 1) ? (vv[e >> 1] >> 16) : (vv[e >> 1] & 0xFFFFu));
-    }
+  auto put = [&](const Planes& pl, uint32_t cw, int d, int sb) {
+    *reinterpret_cast<u32x4*>(sF[sb] + swzN(wrow, 8 * wb + 2 * wq + d)) = dequant8(pl, cw);
   };
 
+  const int kh = wave_k();
   auto compute_store = [&](Acc& acc, int cb, const Stage& S, int sb) {
-    Frags F;
-    Planes pl;
-    read_frags(F, sT[cb], sF[cb], 0);
-    mma_group(acc, F, 0);
+    Frags Fa, Fb;
+    read_frags_natural(Fa, sT[cb], sF[cb], 2 * kh);
+    read_frags_natural(Fb, sT[cb], sF[cb], 2 * kh + 1);
+    mma_group(acc, Fa, 0);
     store_tokens_part(S.T, sT[sb], 0);
     store_tokens_part(S.T, sT[sb], 1);
     const float scale = scale_of(S);
-    mma_group(acc, F, 1);
+    mma_group(acc, Fa, 1);
     store_tokens_part(S.T, sT[sb], 2);
     store_tokens_part(S.T, sT[sb], 3);
-    pl = make_planes(p.tab, scale);
-    mma_group(acc, F, 2);
-    store_tokens_part(S.T, sT[sb], 4);
-    store_tokens_part(S.T, sT[sb], 5);
-    put8(pl, codes_of(S, 0), 0, sb);
-    mma_group(acc, F, 3);
-    store_tokens_part(S.T, sT[sb], 6);
-    store_tokens_part(S.T, sT[sb], 7);
-    put8(pl, codes_of(S, 1), 1, sb);
-    read_frags(F, sT[cb], sF[cb], 1);
-    mma_group(acc, F, 0);
-    put8(pl, codes_of(S, 2), 2, sb);
-    mma_group(acc, F, 1);
-    put8(pl, codes_of(S, 3), 3, sb);
-    mma_group(acc, F, 2);
-    mma_group(acc, F, 3);
+    const Planes pl = quad_planes(lev, scale);
+    mma_group(acc, Fb, 0);
+    put(pl, S.W.code.x, 0, sb);
+    mma_group(acc, Fb, 1);
+    put(pl, S.W.code.y, 1, sb);
   };
 
   auto store_all = [&](const Stage& S, int sb) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) store_tokens_part(S.T, sT[sb], i);
-    const Planes pl = make_planes(p.tab, scale_of(S));
-#pragma unroll
-    for (int q = 0; q < 4; ++q) put8(pl, codes_of(S, q), q, sb);
+    for (int i = 0; i < 4; ++i) store_tokens_part(S.T, sT[sb], i);
+    const Planes pl = quad_planes(lev, scale_of(S));
+    put(pl, S.W.code.x, 0, sb);
+    put(pl, S.W.code.y, 1, sb);
   };
 
   Acc acc;
   acc_zero(acc);
-  Stage S0 = {}, S1 = {};
+  Stage S0, S1;
+  // Prefetch loads are unconditional (a stage index past the end is clamped to the last
+  // stage and the data is never stored): a load under a branch would make the compiler
+  // wait for every load in flight where the branch rejoins.
+  const uint32_t last = nred - 1;
   load(0, S0);
-  if (nred > 1) load(1, S1);
+  load(min(1u, last), S1);
   store_all(S0, 0);
   __syncthreads();
   // two stages per trip (stage it in buffer 0 with it+1 in S1, then it+1 in buffer 1 with
   // it+2 in S0); a single exit keeps the accumulators in one register set
   uint32_t it = 0;
   for (; it + 1 < nred; it += 2) {
-    if (it + 2 < nred) load(it + 2, S0);
+    load(min(it + 2, last), S0);
     compute_store(acc, 0, S1, 1);
     __syncthreads();
-    if (it + 3 < nred) load(it + 3, S1);
+    load(min(it + 3, last), S1);
     compute_store(acc, 1, S0, 0);
     __syncthreads();
   }
   if (it < nred) {   // odd number of stages: the last one is in buffer 0
-    mma_stage(acc, sT[0], sF[0]);
+    mma_stage<true>(acc, sT[0], sF[0]);
     __syncthreads();
   }
 
-  // adapter stages: Gs [M][rp] against A rows (already feature-major: A is [K][r])
-  const rsrc_t rG = make_rsrc(p.Gs, (uint64_t)p.M * p.rp * 2);
+  // adapter stages: Gs [M][rp] against rows of A (feature-major: A is [K][r]).  Columns
+  // j >= r of a row of A hold the next row's values; Gs is zero there.
+  const TokenSrc gs = token_src(p.Gs, (uint64_t)p.M * p.rp * 2, (uint32_t)p.rp, m0);
   const rsrc_t rAd = make_rsrc(p.A, (uint64_t)p.K * p.r * 2);
   for (uint32_t j0 = 0; j0 < (uint32_t)p.rp; j0 += 64) {
     TokenRegs T;
-    load_tokens(T, rG, (uint32_t)p.rp, m0, j0);
-    const int kr = t >> 1, jc = (t & 1) * 32;
-    uint4 a[4];
+    load_tokens(T, gs, j0);
+    const uint32_t aoff = ((k0 + wrow * 2 + wb) * (uint32_t)p.r + j0 + wq * 16) * 2;
+    const uint4 a0 = ld16(rAd, aoff), a1 = ld16(rAd, aoff + 16);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) a[q] = ld16(rAd, ((k0 + kr) * (uint32_t)p.r + j0 + jc + q * 8) * 2);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) store_tokens_part(T, sT[0], i);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) *reinterpret_cast<uint4*>(sF[0] + swzF(kr, (jc >> 3) + q)) = a[q];
+    for (int i = 0; i < 4; ++i) store_tokens_part(T, sT[0], i);
+    *reinterpret_cast<uint4*>(sF[0] + swzF(wrow * 2 + wb, 2 * wq)) = a0;
+    *reinterpret_cast<uint4*>(sF[0] + swzF(wrow * 2 + wb, 2 * wq + 1)) = a1;
     __syncthreads();
-    mma_stage(acc, sT[0], sF[0]);
+    mma_stage<false>(acc, sT[0], sF[0]);
     __syncthreads();
   }
-  store_out(acc, p.dX, p.K, m0, p.M, k0, p.K);
+  if (combine_halves(acc, smem)) store_out(acc, p.dX, p.K, m0, p.M, k0, p.K);
 }
 
 }  // namespace
@@ -194,10 +179,16 @@ hipError_t launch_dx_gemm(const uint16_t* dY, int64_t M, int64_t K, int64_t N, c
              Gs, rp, A, r, dX, nf4_table()};
   const int64_t tiles = ((M + BT - 1) / BT) * ((K + BF - 1) / BF);
   ProfScope ps("k_bwd_dx_nf4_gemm", s);
-  if (w.dq)
-    hipLaunchKernelGGL(k_bwd_dx_nf4_gemm<true>, dim3((unsigned)tiles), dim3(NT), 0, s, p);
+  const dim3 grid((unsigned)tiles), block(NT);
+  const bool ragged = (N % 64) != 0;
+  if (w.dq && !ragged)
+    hipLaunchKernelGGL((k_bwd_dx_nf4_gemm<true, false>), grid, block, 0, s, p);
+  else if (w.dq)
+    hipLaunchKernelGGL((k_bwd_dx_nf4_gemm<true, true>), grid, block, 0, s, p);
+  else if (!ragged)
+    hipLaunchKernelGGL((k_bwd_dx_nf4_gemm<false, false>), grid, block, 0, s, p);
   else
-    hipLaunchKernelGGL(k_bwd_dx_nf4_gemm<false>, dim3((unsigned)tiles), dim3(NT), 0, s, p);
+    hipLaunchKernelGGL((k_bwd_dx_nf4_gemm<false, true>), grid, block, 0, s, p);
   return hipGetLastError();
 }
 
