@@ -164,9 +164,8 @@ FwdWs fwd_layout(void* base, int64_t M, int64_t in, int64_t out, int32_t r) {
   const int64_t Mm = std::max<int64_t>(M, 1);
   FwdWs ws;
   ws.t = lora_problem(gemm_T(nullptr, nullptr, Mm, in, r), epi_none(), kMaxSplits);
-  ws.gv = gemv_plan(in, out);
-  size_t pf = lora_partial_floats(ws.t);
-  if (use_gemv(M)) pf = std::max(pf, gemv_partial_floats(ws.gv, Mm));
+  ws.gv = gemv_plan(Mm, in, out, rp);
+  const size_t pf = use_gemv(M) ? gemv_partial_floats(ws.gv, Mm) : lora_partial_floats(ws.t);
   ws.Ts = c.take<uint16_t>((size_t)Mm * rp);
   ws.partial = c.take<float>(std::max<size_t>(pf, 1));
   ws.bytes = round_up(c.off, 256);
@@ -320,18 +319,20 @@ qlora_status qlora_linear_fwd(const uint16_t* X, int64_t M, const qlora_nf4* w, 
   const FwdWs L = fwd_layout(ws, M, in, out, r);
   const NF4View v = view_of(w);
 
+  if (use_gemv(M)) {
+    // few tokens: one pass over the packed weight that also forms the partials of X A, then
+    // an epilogue that finishes T, Ts and Y
+    QL_HIP(launch_gemv(X, M, in, out, v, A, r, L.gv, L.partial, stream));
+    QL_HIP(launch_gemv_epilogue(L.partial, L.gv, M, out, B, r, scale, Y, T_save, stream));
+    return QLORA_OK;
+  }
   // T = X A (bf16 to T_save) and Ts = bf16(s T) padded to rp columns, then the fused product
   LoraProblem pt = lora_problem(gemm_T(X, A, M, in, r), LoraEpi{T_save, r, 1.0f, L.Ts, rp, scale, nullptr, 0.0f},
                                 kMaxSplits);
   pt.partial = L.partial;
   QL_HIP(launch_lora(pt, nullptr, "k_lora_xa", stream));
   if (pt.splits > 1) QL_HIP(launch_lora_reduce(pt, nullptr, "k_lora_xa_reduce", stream));
-  if (use_gemv(M)) {
-    QL_HIP(launch_gemv(X, M, in, out, v, L.gv, L.partial, stream));
-    QL_HIP(launch_gemv_epilogue(L.partial, L.gv, M, out, L.Ts, rp, B, r, Y, stream));
-  } else {
-    QL_HIP(launch_fwd_gemm(X, M, in, out, v, L.Ts, rp, B, r, Y, stream));
-  }
+  QL_HIP(launch_fwd_gemm(X, M, in, out, v, L.Ts, rp, B, r, Y, stream));
   return QLORA_OK;
 }
 

@@ -77,20 +77,25 @@ hipError_t launch_fwd_gemm(const uint16_t* X, int64_t M, int64_t K, int64_t N, c
                            hipStream_t s);
 
 // ---- fused forward, skinny M <= 16 (gemv.hip) ---------------------------------------------
-// Y[M][N] = bf16( X deq(W)^T + Ts[M][rp] B ): the dequantizing product split over the
-// reduction into fp32 partials, then an epilogue kernel that adds the splits in
-// order and the adapter term.
+// k_fwd_nf4_gemv writes fp32 partials: partial[split][m][n] (X deq(W)^T over `splits` slices
+// of the reduction) and, at float offset tpart, tpartial[aslice][m][j] (X A over `asplits`
+// slices of ka rows); launch_gemv_epilogue forms T, Ts = bf16(s T), T_save = bf16(T) when
+// T_save is not NULL, and Y = bf16( sum of weight partials + Ts B ).
 struct GemvPlan {
   int splits;
   int64_t kb_per_split;
-  int64_t groups;
+  int64_t wgroups, agroups;   // 64-row weight groups, 64-column adapter groups
+  int64_t npad;               // weight partial row length (wgroups * 64)
+  int64_t ka;                 // rows of A per adapter slice
+  int asplits;
+  size_t tpart;               // float offset of the adapter partials
 };
-GemvPlan gemv_plan(int64_t K, int64_t N);
+GemvPlan gemv_plan(int64_t M, int64_t K, int64_t N, int64_t rp);
 size_t gemv_partial_floats(const GemvPlan& pl, int64_t M);
-hipError_t launch_gemv(const uint16_t* X, int64_t M, int64_t K, int64_t N, const NF4View& w, const GemvPlan& pl,
-                       float* partial, hipStream_t s);
-hipError_t launch_gemv_epilogue(const float* partial, const GemvPlan& pl, int64_t M, int64_t N, const uint16_t* Ts,
-                                int64_t rp, const uint16_t* B, int64_t r, uint16_t* Y, hipStream_t s);
+hipError_t launch_gemv(const uint16_t* X, int64_t M, int64_t K, int64_t N, const NF4View& w, const uint16_t* A,
+                       int64_t r, const GemvPlan& pl, float* partial, hipStream_t s);
+hipError_t launch_gemv_epilogue(const float* partial, const GemvPlan& pl, int64_t M, int64_t N, const uint16_t* B,
+                                int64_t r, float scale, uint16_t* Y, uint16_t* T_save, hipStream_t s);
 
 // ---- backward dX (dx_gemm.hip) --------------------------------------------------------------
 // dX[M][K] = bf16( dY[M][N] deq(W) + Gs[M][rp] A^T ), A [K][r].
