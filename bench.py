@@ -3,13 +3,14 @@
 
 Headline workload: the 7B-shaped attention projection, W 4096x4096 (bf16,
 N(0, 0.02^2)) quantized to NF4 with double quantization, LoRA rank 64
-(alpha 16, s = 0.25), X of 2048 tokens (batch 4 x seq 512).  One step is the
-whole hot path on one batch: quantize + double-quantize the weight, forward
-(X A, fused dequant GEMM with the adapter term), backward (dY B^T, fused
-dequant dX GEMM, dA, dB).  `value` counts the forward+backward FLOPs
-4 M in out + 6 M r (in + out) (no dW; dequantization and quantization not
-counted) per step time, inputs already resident in HBM.  Four independent input
-sets are rotated so consecutive steps do not hit in the 256 MB Infinity Cache.
+(alpha 16, s = 0.25), X of 2048 tokens (batch 4 x seq 512).  The frozen weight is
+quantized once per input set, outside the timed region (as in QLoRA training, where
+the base weight is quantized once); one step is the forward (X A, fused dequant
+GEMM with the adapter term) and the backward (dY B^T, fused dequant dX GEMM, dA,
+dB) on one batch.  `value` counts the forward+backward FLOPs
+4 M in out + 6 M r (in + out) (no dW; dequantization not counted) per step time,
+inputs already resident in HBM.  Four independent input sets are rotated so
+consecutive steps do not hit in the 256 MB Infinity Cache.
 
 Also reported:
   roofline     -- the dominant kernel's algorithmic FLOPs per launch over its
@@ -18,8 +19,10 @@ Also reported:
   gemv         -- the skinny-token forward at the 65B shapes (8192->22016 and
                   22016->8192, M in {1,4,16}): packed-weight GB/s against 8 TB/s,
                   rotating 6 weight copies (> 512 MB) per shape;
+  quantize     -- quantize + double-quantize of the headline weight (timed apart):
+                  bytes moved (bf16 in, codes and constants out) over time;
   cpu_baseline -- the float64 NumPy oracle doing one full step of the headline
-                  workload on the host cores.
+                  workload (dequantize, forward, backward) on the host cores.
 
 Prints one JSON line.
 """
@@ -50,7 +53,7 @@ KERNEL_SOURCES = {
     "k_fwd_nf4_gemm": ["fwd_gemm.hip", "gemm_core.h", "common.h"],
     "k_bwd_dx_nf4_gemm": ["dx_gemm.hip", "gemm_core.h", "common.h"],
     "k_nf4_quantize": ["quant.hip", "common.h"],
-    "k_fwd_nf4_gemv": ["gemv.hip", "common.h"],
+    "k_fwd_nf4_gemv": ["gemv.hip", "gemm_core.h", "common.h"],
 }
 
 
@@ -124,7 +127,7 @@ def main():
               "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
               "data": "synthetic (seeded Gaussian, LLaMA-7B layer shape)"}
     result["config"] = {"workload": "QLoRA linear 4096->4096, 2048 tokens, NF4 block 64 + double quant 256, "
-                                    "LoRA r=64 alpha=16; step = quantize + forward + backward",
+                                    "LoRA r=64 alpha=16; step = forward + backward on the quantized weight",
                         "M": M, "in": din, "out": dout, "r": r, "alpha": alpha, "input_sets": args.sets,
                         "flops_per_step": flops}
 
@@ -147,9 +150,15 @@ def main():
         ws = torch.empty(max(Q.qlora_quantize_workspace(dout, din), Q.qlora_fwd_workspace(M, din, dout, r),
                              Q.qlora_bwd_workspace(M, din, dout, r)), dtype=torch.uint8, device=dev)
 
-        def step(i):
+        def quantize(i):
             d = sets[i % len(sets)]
             Q.qlora_quantize_nf4(d["W"], True, out=d["w"], workspace=ws)
+
+        for i in range(len(sets)):
+            quantize(i)
+
+        def step(i):
+            d = sets[i % len(sets)]
             Q.qlora_linear_fwd(d["X"], d["w"], d["A"], d["B"], s, Y=d["Y"], T_save=d["T"], workspace=ws)
             Q.qlora_linear_bwd(d["dY"], d["X"], d["T"], d["w"], d["A"], d["B"], s, dX=d["dX"], dA=d["dA"],
                                dB=d["dB"], workspace=ws)
@@ -192,9 +201,31 @@ def main():
                               "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)",
                               "algorithmic_bytes": algo_bytes,
                               "flops_per_launch": algo[dom], "avg_us": kern[dom]["avg_us"]}
-        fb_us = sum(v["us_per_step"] for k, v in kern.items() if k not in ("k_nf4_quantize", "k_dq_mean",
-                                                                              "k_dq_encode", "k_fill_u32"))
+        fb_us = sum(v["us_per_step"] for v in kern.values())
         result["fwd_bwd_kernel_tflops"] = flops / (fb_us * 1e-6) / 1e12
+
+        # quantize + double-quantize, timed apart (bf16 weight in; codes, 8-bit constants,
+        # per-256 scales and the mean out)
+        qbytes = 2 * din * dout + weight_bytes(din, dout)
+        for i in range(3):
+            quantize(i)
+        torch.cuda.synchronize()
+        ev0.record()
+        for i in range(args.steps):
+            quantize(i)
+        ev1.record()
+        torch.cuda.synchronize()
+        qus = 1e3 * ev0.elapsed_time(ev1) / args.steps
+        Q.qlora_profile_enable(True)
+        Q.qlora_profile_read(reset=True)
+        for i in range(args.steps):
+            quantize(i)
+        torch.cuda.synchronize()
+        qprof = Q.qlora_profile_read(reset=True)
+        Q.qlora_profile_enable(False)
+        result["quantize"] = {"us_per_call": qus, "bytes": qbytes, "GBps": qbytes / (qus * 1e-6) / 1e9,
+                              "peak_GBps": PEAK_HBM_GBPS,
+                              "kernels_us": {k: 1e3 * t / n for k, (n, t) in qprof.items()}}
         del sets, ws
         torch.cuda.empty_cache()
 
@@ -259,7 +290,8 @@ def bench_gemv(Q, workloads, torch, dev, iters):
 
 
 def cpu_baseline(M, din, dout, r, alpha, flops):
-    """The oracle as it stands: one full step (quantize + forward + backward) in float64 NumPy."""
+    """The oracle as it stands: one step (dequantize + forward + backward) in float64 NumPy, the
+    weight quantized once beforehand."""
     import numpy as np
 
     import workloads
@@ -267,10 +299,10 @@ def cpu_baseline(M, din, dout, r, alpha, flops):
 
     lin = workloads.Linear("proj", M, din, dout, r, alpha)
     inp = workloads.linear_inputs(2, lin)
+    q = nf4.quantize(inp.W, double_quant=True)
     reps, total = 0, 0.0
     while reps < 5 and (reps == 0 or total < 10.0):   # about 10 s of CPU work
         t0 = time.perf_counter()
-        q = nf4.quantize(inp.W, double_quant=True)
         Wd = nf4.dequantize(q, (dout, din))
         linear.forward(inp.X, Wd, inp.A, inp.B, lin.scale)
         linear.backward(inp.dY, inp.X, Wd, inp.A, inp.B, lin.scale)
@@ -286,7 +318,7 @@ def cpu_baseline(M, din, dout, r, alpha, flops):
         pass
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads or len(os.sched_getaffinity(0)),
             "kind": "oracle", "seconds_per_step": dt, "repeats": reps,
-            "sample": "full steps of the headline workload (quantize + dequantize + forward + backward), "
+            "sample": "full steps of the headline workload (dequantize + forward + backward), "
                       "float64 NumPy, BLAS threads = cores, averaged over the repeats"}
 
 

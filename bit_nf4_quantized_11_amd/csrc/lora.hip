@@ -6,60 +6,100 @@
 // partial tile; a second kernel adds the partials in split order (so the result
 // does not depend on timing) and writes the bf16 / fp32 outputs.  The hand-off goes
 // through a kernel boundary: on this GPU each XCD has its own L2, and an in-kernel
-// device-scope fence would write back and invalidate it.  Tiles are 64 x 64, 64 deep per step, on
-// v_mfma_f32_16x16x32_bf16; both operands go through LDS with the reduction
-// index contiguous, whatever their layout in memory, and the next step's tiles are
-// prefetched into registers while the current step computes.
+// device-scope fence would write back and invalidate it.
+//
+// Tiles are 64 x 64, 64 deep per step, on v_mfma_f32_16x16x32_bf16, with both operand
+// tiles double-buffered in LDS and the next step's loads in flight while the current
+// step computes.  An operand stored contiguously along the reduction ("KC") is kept as
+// [row][k] and read with 16-byte LDS loads; one stored contiguously along its row index
+// is kept as stored ([k][row]) and read with transposing loads (ds_read_b64_tr_b16).
+// Loads go through raw buffer resources with explicit masks: elements past the ends of
+// the reduction or of the rows read as zero.
 #include "common.h"
+#include "gemm_core.h"
 #include "kernels.h"
 
 namespace qlora {
 
 namespace {
 
-constexpr int TI = 64, TJ = 64, TK = 64, LDK = TK + 8;   // LDS row: 72 bf16 = 144 bytes
+using gemm::i16x4;
+using gemm::ld16;
+using gemm::make_rsrc;
+using gemm::rsrc_t;
 
-// 64 rows x 64 reduction elements of an operand, staged per thread as two 8-element
-// vectors.  K_CONTIG: vectors along the reduction; otherwise along the rows.
-template <bool K_CONTIG>
-struct Tile {
-  uint4 v[2];
-  __device__ __forceinline__ void load(const uint16_t* __restrict__ P, int64_t s_row, int64_t s_k, int64_t row0,
-                                       int64_t nrow, int64_t k0, int64_t kend) {
-    const int t = threadIdx.x;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      v[h] = make_uint4(0, 0, 0, 0);
-      if (K_CONTIG) {
-        const int row = (t >> 3) + 32 * h, kc = (t & 7) * 8;
-        const int64_t gr = row0 + row, gk = k0 + kc;
-        if (gr < nrow && gk < kend) v[h] = *reinterpret_cast<const uint4*>(P + gr * s_row + gk);   // kend % 8 == 0
-      } else {
-        const int k = (t >> 3) + 32 * h, rc = (t & 7) * 8;
-        const int64_t gk = k0 + k, gr = row0 + rc;
-        if (gk < kend && gr < nrow) v[h] = *reinterpret_cast<const uint4*>(P + gk * s_k + gr);   // nrow % 8 == 0
-      }
-    }
-  }
-  __device__ __forceinline__ void store(uint16_t* __restrict__ lds) const {
-    const int t = threadIdx.x;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      if (K_CONTIG) {
-        const int row = (t >> 3) + 32 * h, kc = (t & 7) * 8;
-        *reinterpret_cast<uint4*>(lds + row * LDK + kc) = v[h];
-      } else {
-        const int k = (t >> 3) + 32 * h, rc = (t & 7) * 8;
-        const uint32_t w[4] = {v[h].x, v[h].y, v[h].z, v[h].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          lds[(rc + 2 * e) * LDK + k] = (uint16_t)(w[e] & 0xFFFFu);
-          lds[(rc + 2 * e + 1) * LDK + k] = (uint16_t)(w[e] >> 16);
-        }
-      }
-    }
-  }
+constexpr int TI = 64, TJ = 64, TK = 64;
+
+// [row][k] tile (128-byte rows of eight 16-byte chunks): chunk c of row r at c ^ ((r >> 1) & 7);
+// 16 consecutive rows of one chunk (a fragment read) and 2 rows x 8 chunks (a store) are
+// conflict-free.
+__device__ __forceinline__ int kcpos(int row, int c) { return row * 64 + ((c ^ ((row >> 1) & 7)) << 3); }
+// [k][row] tile: chunk q of k-row k at q ^ 2 f(k), f(k) = ((k >> 1) & 1) | ((k >> 2) & 2):
+// transposing reads (4 k-rows x 32 bytes per 16 lanes, two such quads 8 apart per 32 lanes)
+// and stores (2 k-rows x 8 chunks) are conflict-free.
+__device__ __forceinline__ int trpos(int k, int q) {
+  const int f = ((k >> 1) & 1) | ((k >> 2) & 2);
+  return k * 64 + ((q ^ (f << 1)) << 3);
+}
+
+// One operand of a product: element (o, k) (o = row index i or column index j) at
+// P[o * ld + k] when KC, else P[k * ld + o]; o < nout, k < K.
+struct Operand {
+  rsrc_t r;
+  uint32_t end;
+  int64_t ld, nout;
 };
+
+template <bool KC>
+__device__ __forceinline__ void load_panel(uint4 (&v)[2], const Operand& op, int64_t o0, int64_t k0, int64_t kend) {
+  const int t = threadIdx.x;
+  const int lr = t >> 3, lc = t & 7;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int mr = lr + 32 * h;
+    int64_t o, k;
+    if constexpr (KC) {
+      o = o0 + mr;
+      k = k0 + lc * 8;
+    } else {
+      k = k0 + mr;
+      o = o0 + lc * 8;
+    }
+    const bool valid = o < op.nout && k < kend;   // nout % 8 == 0 (!KC), kend % 8 == 0 (KC)
+    const int64_t off = KC ? (o * op.ld + k) * 2 : (k * op.ld + o) * 2;
+    v[h] = ld16(op.r, valid ? (uint32_t)off : op.end);
+  }
+}
+
+template <bool KC>
+__device__ __forceinline__ void store_panel(const uint4 (&v)[2], uint16_t* __restrict__ lds) {
+  const int t = threadIdx.x;
+  const int lr = t >> 3, lc = t & 7;
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    *reinterpret_cast<uint4*>(lds + (KC ? kcpos(lr + 32 * h, lc) : trpos(lr + 32 * h, lc))) = v[h];
+}
+
+// 16x16x32 operand: rows ob + lane % 16, reduction ks*32 + 8 (lane / 16) .. +7
+template <bool KC>
+__device__ __forceinline__ u32x4 read_frag(const uint16_t* __restrict__ lds, int ob, int ks) {
+  const int lane = threadIdx.x & 63;
+  if constexpr (KC) {
+    return *reinterpret_cast<const u32x4*>(lds + kcpos(ob + (lane & 15), ks * 4 + (lane >> 4)));
+  } else {
+    const int j = lane & 15, G = lane >> 4;
+    const int kr = ks * 32 + G * 8 + (j >> 2);
+    const int col = ob + (j & 3) * 4;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(lds + trpos(kr, col >> 3) + (col & 7)));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(lds + trpos(kr + 4, col >> 3) + (col & 7)));
+    const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
+    u32x4 o;
+    o.x = a.x; o.y = a.y; o.z = b.x; o.w = b.y;
+    return o;
+  }
+}
 
 __device__ __forceinline__ void epi_write(const LoraEpi& ep, int64_t I, int64_t J, int64_t i, int64_t j, float sum) {
   if (i >= I) return;
@@ -74,8 +114,8 @@ __device__ __forceinline__ void epi_write(const LoraEpi& ep, int64_t I, int64_t 
 
 template <bool A_KC, bool B_KC>
 __global__ __launch_bounds__(256) void k_lora_gemm(LoraProblem p0, LoraProblem p1, int nprob) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[TI * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[TJ * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][TI * TK];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][TJ * TK];
 
   // which problem, tile and split this workgroup owns
   int64_t wg = blockIdx.x;
@@ -89,6 +129,13 @@ __global__ __launch_bounds__(256) void k_lora_gemm(LoraProblem p0, LoraProblem p
   const int64_t i0 = ti * TI, j0 = tj * TJ;
   const int64_t kbeg = (int64_t)split * P.k_per_split;
   const int64_t kend = min(g.K, kbeg + P.k_per_split);
+  const int nsteps = (int)((kend - kbeg + TK - 1) / TK);
+
+  // operand extents (largest element index + 1) bound the buffer resources
+  const uint64_t a_ext = (uint64_t)((g.I - 1) * g.a_si + (g.K - 1) * g.a_sk + 1);
+  const uint64_t b_ext = (uint64_t)((g.K - 1) * g.b_sk + (g.J - 1) * g.b_sj + 1);
+  const Operand oa{make_rsrc(g.A, a_ext * 2), (uint32_t)(a_ext * 2), A_KC ? g.a_si : g.a_sk, g.I};
+  const Operand ob{make_rsrc(g.B, b_ext * 2), (uint32_t)(b_ext * 2), B_KC ? g.b_sj : g.b_sk, g.J};
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wi = wave & 1, wj = wave >> 1;
@@ -98,34 +145,33 @@ __global__ __launch_bounds__(256) void k_lora_gemm(LoraProblem p0, LoraProblem p
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  Tile<A_KC> ta;
-  Tile<B_KC> tb;
-  if (kbeg < kend) {
-    ta.load(g.A, A_KC ? g.a_si : g.a_sk, A_KC ? 1 : g.a_sk, i0, g.I, kbeg, kend);
-    tb.load(g.B, B_KC ? g.b_sj : g.b_sk, B_KC ? 1 : g.b_sk, j0, g.J, kbeg, kend);
-  }
-  for (int64_t k0 = kbeg; k0 < kend; k0 += TK) {
-    ta.store(sA);
-    tb.store(sB);
-    __syncthreads();
-    if (k0 + TK < kend) {   // prefetch the next step while this one computes
-      ta.load(g.A, A_KC ? g.a_si : g.a_sk, A_KC ? 1 : g.a_sk, i0, g.I, k0 + TK, kend);
-      tb.load(g.B, B_KC ? g.b_sj : g.b_sk, B_KC ? 1 : g.b_sk, j0, g.J, k0 + TK, kend);
-    }
+  uint4 va[2], vb[2];
+  load_panel<A_KC>(va, oa, i0, kbeg, kend);
+  load_panel<B_KC>(vb, ob, j0, kbeg, kend);
+  store_panel<A_KC>(va, sA[0]);
+  store_panel<B_KC>(vb, sB[0]);
+  __syncthreads();
+  // step s computes from buffer s % 2 while step s + 1 loads (a step past the end reloads the
+  // last one; its buffer is never read)
+  for (int st = 0; st < nsteps; ++st) {
+    const int64_t kn = kbeg + (int64_t)min(st + 1, nsteps - 1) * TK;
+    load_panel<A_KC>(va, oa, i0, kn, kend);
+    load_panel<B_KC>(vb, ob, j0, kn, kend);
+    const int cb = st & 1;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       u32x4 af[2], bfr[2];
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
-        af[a] = *reinterpret_cast<const u32x4*>(sA + (wi * 32 + a * 16 + (lane & 15)) * LDK + ks * 32 + (lane >> 4) * 8);
+      for (int a = 0; a < 2; ++a) af[a] = read_frag<A_KC>(sA[cb], wi * 32 + a * 16, ks);
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
-        bfr[b] = *reinterpret_cast<const u32x4*>(sB + (wj * 32 + b * 16 + (lane & 15)) * LDK + ks * 32 + (lane >> 4) * 8);
+      for (int b = 0; b < 2; ++b) bfr[b] = read_frag<B_KC>(sB[cb], wj * 32 + b * 16, ks);
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int b = 0; b < 2; ++b) acc[a][b] = mfma16(af[a], bfr[b], acc[a][b]);
     }
+    store_panel<A_KC>(va, sA[cb ^ 1]);
+    store_panel<B_KC>(vb, sB[cb ^ 1]);
     __syncthreads();
   }
 
@@ -190,8 +236,8 @@ LoraProblem lora_problem(const SmallGemm& g, const LoraEpi& ep, int max_splits) 
   p.tiles_j = (g.J + TJ - 1) / TJ;
   const int64_t tiles = p.tiles_i * p.tiles_j;
   const int64_t ksteps = (g.K + TK - 1) / TK;
-  int64_t s = (256 + tiles - 1) / tiles;   // about one workgroup per compute unit
-  if (s > ksteps / 2) s = ksteps / 2;      // keep at least 2 steps per split
+  int64_t s = (384 + tiles - 1) / tiles;   // about 1.5 workgroups per compute unit
+  if (s > ksteps / 4) s = ksteps / 4;      // keep at least 4 steps per split
   if (s > max_splits) s = max_splits;
   if (s < 1) s = 1;
   int64_t kps = (ksteps + s - 1) / s * TK;

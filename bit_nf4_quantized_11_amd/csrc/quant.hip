@@ -17,17 +17,33 @@ namespace {
 
 constexpr int kThreads = 256;
 
-__device__ __forceinline__ uint32_t nf4_encode(float x, const NF4Table& t) {
+// The 15 thresholds held in VGPRs (loaded once per thread): a data-dependent index into the
+// kernel-argument table would become a dependent memory load per search level.
+struct Thr {
+  float v[15];
+};
+
+__device__ __forceinline__ Thr thr_regs(const NF4Table& t) {
+  Thr h;
+#pragma unroll
+  for (int k = 0; k < 15; ++k) {
+    h.v[k] = t.thr[k];
+    asm volatile("" : "+v"(h.v[k]));
+  }
+  return h;
+}
+
+__device__ __forceinline__ uint32_t nf4_encode(float x, const Thr& t) {
   // code = #{k : x > thr[k]} by a 4-level binary search over the sorted thresholds
-  const uint32_t b3 = x > t.thr[7];
-  const float t2 = b3 ? t.thr[11] : t.thr[3];
-  const uint32_t b2 = x > t2;
-  const float t1 = b3 ? (b2 ? t.thr[13] : t.thr[9]) : (b2 ? t.thr[5] : t.thr[1]);
-  const uint32_t b1 = x > t1;
-  const float t0 = b3 ? (b2 ? (b1 ? t.thr[14] : t.thr[12]) : (b1 ? t.thr[10] : t.thr[8]))
-                      : (b2 ? (b1 ? t.thr[6] : t.thr[4]) : (b1 ? t.thr[2] : t.thr[0]));
-  const uint32_t b0 = x > t0;
-  return (b3 << 3) | (b2 << 2) | (b1 << 1) | b0;
+  const bool b3 = x > t.v[7];
+  const bool b2 = x > (b3 ? t.v[11] : t.v[3]);
+  const float t1a = b2 ? t.v[13] : t.v[9], t1b = b2 ? t.v[5] : t.v[1];
+  const bool b1 = x > (b3 ? t1a : t1b);
+  const float q3 = b1 ? t.v[14] : t.v[12], q2 = b1 ? t.v[10] : t.v[8];
+  const float q1 = b1 ? t.v[6] : t.v[4], q0 = b1 ? t.v[2] : t.v[0];
+  const float t0 = b3 ? (b2 ? q3 : q2) : (b2 ? q1 : q0);
+  const bool b0 = x > t0;
+  return ((uint32_t)b3 << 3) | ((uint32_t)b2 << 2) | ((uint32_t)b1 << 1) | (uint32_t)b0;
 }
 
 // Eight lanes per 64-block, eight consecutive weights per lane (one 16-byte load, one
@@ -42,6 +58,7 @@ __global__ __launch_bounds__(kThreads) void k_nf4_quantize(const uint16_t* __res
   if (dq) lhist[threadIdx.x] = 0ull;
   __syncthreads();
   const int sub = threadIdx.x & 7;
+  const Thr thr = thr_regs(tab);
   const int64_t nblk = (numel + 63) >> 6;
   const int64_t stride = (int64_t)gridDim.x * (kThreads / 8);
   for (int64_t blk = (int64_t)blockIdx.x * (kThreads / 8) + (threadIdx.x >> 3); blk < nblk; blk += stride) {
@@ -68,7 +85,7 @@ __global__ __launch_bounds__(kThreads) void k_nf4_quantize(const uint16_t* __res
     const float inv = m ? (float)(1.0 / (double)a) : 0.0f;
     uint32_t c[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = nf4_encode(__fmul_rn(bf16_to_f32(h[i]), inv), tab);
+    for (int i = 0; i < 8; ++i) c[i] = nf4_encode(__fmul_rn(bf16_to_f32(h[i]), inv), thr);
     uint32_t packed = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) packed |= (c[i] | (c[i + 4] << 4)) << (8 * i);
