@@ -127,7 +127,7 @@ qlora_status check_linear(int64_t M, const qlora_nf4* w, int32_t r) {
 }
 
 // ---- workspace layouts ----------------------------------------------------------------------
-constexpr int kMaxSplits = 16;
+constexpr int kMaxSplits = kMaxLoraSplits;
 
 SmallGemm gemm_T(const uint16_t* X, const uint16_t* A, int64_t M, int64_t in, int64_t r) {
   // T[m][j] = sum_k X[m][k] A[k][j]

@@ -63,6 +63,7 @@ struct LoraProblem {
   int splits;
   float* partial;        // splits > 1: tiles * splits * 64*64 floats of workspace
 };
+constexpr int kMaxLoraSplits = 16;   // the reduce kernel sums at most this many partials
 LoraProblem lora_problem(const SmallGemm& g, const LoraEpi& ep, int max_splits);
 size_t lora_partial_floats(const LoraProblem& p);
 // one launch for p0, or for p0 and p1 together (same operand layouts); with splits > 1

@@ -9,8 +9,7 @@
 // device-scope fence would write back and invalidate it.
 //
 // Tiles are 64 x 64, 64 deep per step, on v_mfma_f32_16x16x32_bf16, with both operand
-// tiles double-buffered in LDS and the next step's loads in flight while the current
-// step computes.  An operand stored contiguously along the reduction ("KC") is kept as
+// tiles double-buffered in LDS; the loads of up to eight steps are in flight at once.  An operand stored contiguously along the reduction ("KC") is kept as
 // [row][k] and read with 16-byte LDS loads; one stored contiguously along its row index
 // is kept as stored ([k][row]) and read with transposing loads (ds_read_b64_tr_b16).
 // Loads go through raw buffer resources with explicit masks: elements past the ends of
@@ -29,6 +28,7 @@ using gemm::make_rsrc;
 using gemm::rsrc_t;
 
 constexpr int TI = 64, TJ = 64, TK = 64;
+constexpr int CH = 8;   // steps per batch of loads (even: the LDS buffer of step q is q % 2)
 
 // [row][k] tile (128-byte rows of eight 16-byte chunks): chunk c of row r at c ^ ((r >> 1) & 7);
 // 16 consecutive rows of one chunk (a fragment read) and 2 rows x 8 chunks (a store) are
@@ -145,34 +145,37 @@ __global__ __launch_bounds__(256) void k_lora_gemm(LoraProblem p0, LoraProblem p
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  uint4 va[2], vb[2];
-  load_panel<A_KC>(va, oa, i0, kbeg, kend);
-  load_panel<B_KC>(vb, ob, j0, kbeg, kend);
-  store_panel<A_KC>(va, sA[0]);
-  store_panel<B_KC>(vb, sB[0]);
-  __syncthreads();
-  // step s computes from buffer s % 2 while step s + 1 loads (a step past the end reloads the
-  // last one; its buffer is never read)
-  for (int st = 0; st < nsteps; ++st) {
-    const int64_t kn = kbeg + (int64_t)min(st + 1, nsteps - 1) * TK;
-    load_panel<A_KC>(va, oa, i0, kn, kend);
-    load_panel<B_KC>(vb, ob, j0, kn, kend);
-    const int cb = st & 1;
+  // The loads of up to CH steps are issued together (a step past the split's end reads
+  // zeros without touching memory), so a workgroup waits for memory once per CH steps;
+  // the LDS tiles are double-buffered with one barrier per step.
+  for (int c0 = 0; c0 < nsteps; c0 += CH) {
+    uint4 va[CH][2], vb[CH][2];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      u32x4 af[2], bfr[2];
-#pragma unroll
-      for (int a = 0; a < 2; ++a) af[a] = read_frag<A_KC>(sA[cb], wi * 32 + a * 16, ks);
-#pragma unroll
-      for (int b = 0; b < 2; ++b) bfr[b] = read_frag<B_KC>(sB[cb], wj * 32 + b * 16, ks);
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b) acc[a][b] = mfma16(af[a], bfr[b], acc[a][b]);
+    for (int q = 0; q < CH; ++q) {
+      const int64_t k = kbeg + (int64_t)(c0 + q) * TK;
+      load_panel<A_KC>(va[q], oa, i0, k, kend);
+      load_panel<B_KC>(vb[q], ob, j0, k, kend);
     }
-    store_panel<A_KC>(va, sA[cb ^ 1]);
-    store_panel<B_KC>(vb, sB[cb ^ 1]);
-    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+      if (c0 + q >= nsteps) break;
+      const int cb = q & 1;
+      store_panel<A_KC>(va[q], sA[cb]);
+      store_panel<B_KC>(vb[q], sB[cb]);
+      __syncthreads();
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        u32x4 af[2], bfr[2];
+#pragma unroll
+        for (int a = 0; a < 2; ++a) af[a] = read_frag<A_KC>(sA[cb], wi * 32 + a * 16, ks);
+#pragma unroll
+        for (int b = 0; b < 2; ++b) bfr[b] = read_frag<B_KC>(sB[cb], wj * 32 + b * 16, ks);
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int b = 0; b < 2; ++b) acc[a][b] = mfma16(af[a], bfr[b], acc[a][b]);
+      }
+    }
   }
 
   // acc[a][b][v] = C[i = wi*32 + a*16 + 4*(lane/16) + v][j = wj*32 + b*16 + lane%16]
@@ -211,13 +214,20 @@ __global__ __launch_bounds__(256) void k_lora_reduce(LoraProblem p0, LoraProblem
   const int e = (int)(idx - tile * (TI * TJ / 4)) * 4;
   const int64_t ti = tile / P.tiles_j, tj = tile - ti * P.tiles_j;
   const float* base = P.partial + tile * P.splits * (TI * TJ) + e;
-  float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int sp = 0; sp < P.splits; ++sp) {
-    const float4 v = *reinterpret_cast<const float4*>(base + sp * (TI * TJ));
-    sum.x = __fadd_rn(sum.x, v.x);
-    sum.y = __fadd_rn(sum.y, v.y);
-    sum.z = __fadd_rn(sum.z, v.z);
-    sum.w = __fadd_rn(sum.w, v.w);
+  // every split's value is loaded before the first add (one memory latency, not splits)
+  float4 v[kMaxLoraSplits];
+#pragma unroll
+  for (int sp = 0; sp < kMaxLoraSplits; ++sp)
+    v[sp] = *reinterpret_cast<const float4*>(base + min(sp, P.splits - 1) * (TI * TJ));
+  float4 sum = v[0];
+#pragma unroll
+  for (int sp = 1; sp < kMaxLoraSplits; ++sp) {
+    if (sp < P.splits) {
+      sum.x = __fadd_rn(sum.x, v[sp].x);
+      sum.y = __fadd_rn(sum.y, v[sp].y);
+      sum.z = __fadd_rn(sum.z, v[sp].z);
+      sum.w = __fadd_rn(sum.w, v[sp].w);
+    }
   }
   const int64_t i = ti * TI + e / TJ, j = tj * TJ + e % TJ;
   epi_write(P.ep, P.g.I, P.g.J, i, j + 0, sum.x);
@@ -236,9 +246,10 @@ LoraProblem lora_problem(const SmallGemm& g, const LoraEpi& ep, int max_splits) 
   p.tiles_j = (g.J + TJ - 1) / TJ;
   const int64_t tiles = p.tiles_i * p.tiles_j;
   const int64_t ksteps = (g.K + TK - 1) / TK;
-  int64_t s = (384 + tiles - 1) / tiles;   // about 1.5 workgroups per compute unit
+  int64_t s = (256 + tiles - 1) / tiles;   // about one workgroup per compute unit
   if (s > ksteps / 4) s = ksteps / 4;      // keep at least 4 steps per split
   if (s > max_splits) s = max_splits;
+  if (s > kMaxLoraSplits) s = kMaxLoraSplits;
   if (s < 1) s = 1;
   int64_t kps = (ksteps + s - 1) / s * TK;
   p.splits = (int)((g.K + kps - 1) / kps);

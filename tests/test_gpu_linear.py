@@ -121,6 +121,31 @@ def test_forward_backward_deterministic():
         assert torch.equal(a[k], b[k]), k
 
 
+def test_shared_workspace():
+    """One workspace serves quantize, forward and backward of two shapes in turn (split
+    rank-r products on both): every result equals the one computed with fresh workspaces."""
+    require_gpu()
+    shapes = [workloads.custom_linear(600, 1024, 768, 64, seed=7), workloads.custom_linear(300, 512, 1024, 16, seed=8)]
+    need = 0
+    for inp in shapes:
+        l = inp.spec
+        need = max(need, Q.qlora_quantize_workspace(l.d_out, l.d_in), Q.qlora_fwd_workspace(l.M, l.d_in, l.d_out, l.r),
+                   Q.qlora_bwd_workspace(l.M, l.d_in, l.d_out, l.r))
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    for rep in range(2):
+        for inp in shapes:
+            l = inp.spec
+            log("shared workspace", rep, f"M={l.M} in={l.d_in} out={l.d_out} r={l.r}")
+            ref = _run(inp)
+            q = Q.qlora_quantize_nf4(dev_bf16(inp.W), workspace=ws)
+            X, A, B, dY = dev_bf16(inp.X), dev_bf16(inp.A), dev_bf16(inp.B), dev_bf16(inp.dY)
+            Y, T = Q.qlora_linear_fwd(X, q, A, B, l.scale, workspace=ws)
+            dX, dA, dB = Q.qlora_linear_bwd(dY, X, T, q, A, B, l.scale, workspace=ws)
+            torch.cuda.synchronize()
+            for k, v in (("Y", Y), ("T", T), ("dX", dX), ("dA", dA), ("dB", dB)):
+                assert torch.equal(v, ref[k]), k
+
+
 def test_c2_full():
     lin = workloads.CONFIGS[2].linears[0]
     _check_full(workloads.linear_inputs(2, lin), label="C2")
