@@ -21,6 +21,10 @@ Also reported:
                   rotating 6 weight copies (> 512 MB) per shape;
   quantize     -- quantize + double-quantize of the headline weight (timed apart):
                   bytes moved (bf16 in, codes and constants out) over time;
+  mlp_7b, stack_65b -- forward+backward TFLOP/s over the 7B MLP pair (M = 4096)
+                  and over the 65B layer stack (80 layers x 7 linears, M = 2048,
+                  all 33 GB of NF4 weight resident), forward layer 0 first, then
+                  the backward in reverse;
   cpu_baseline -- the float64 NumPy oracle doing one full step of the headline
                   workload (dequantize, forward, backward) on the host cores.
 
@@ -84,7 +88,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemv", action="store_true")
     ap.add_argument("--gemv-iters", type=int, default=50)
-    ap.add_argument("--only", choices=["all", "headline", "gemv", "copy"], default="all",
+    ap.add_argument("--no-layers", action="store_true", help="skip the 7B MLP pair and the 65B layer stack")
+    ap.add_argument("--layer-steps", type=int, default=3, help="timed steps of the 7B MLP pair and the 65B stack")
+    ap.add_argument("--only", choices=["all", "headline", "gemv", "layers", "copy"], default="all",
                     help="restrict the run (for profiling single kernels); 'copy' runs a plain device copy of "
                          "known size, the reference for scaling hardware byte counters")
     return ap.parse_args()
@@ -232,6 +238,10 @@ def main():
     if args.only in ("all", "gemv") and not args.no_gemv:
         result["gemv"] = bench_gemv(Q, workloads, torch, dev, args.gemv_iters)
 
+    if args.only in ("all", "layers") and not args.no_layers:
+        result["mlp_7b"] = bench_layers(Q, workloads, torch, dev, 3, args.layer_steps, 1)
+        result["stack_65b"] = bench_layers(Q, workloads, torch, dev, 5, args.layer_steps, 1)
+
     if args.only in ("all", "headline") and not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(M, din, dout, r, alpha, flops)
 
@@ -286,6 +296,99 @@ def bench_gemv(Q, workloads, torch, dev, iters):
     out["weight_GBps_min"] = worst
     out["weight_GBps_max"] = best
     out["frac_min"] = worst / PEAK_HBM_GBPS
+    return out
+
+
+def bench_layers(Q, workloads, torch, dev, cfg_idx, steps, warmup):
+    """Large-token forward+backward over a whole configuration: the 7B MLP pair
+    (4096->11008 and 11008->4096, 0.1% x20 outliers, M = 4096) or the 65B layer stack
+    (80 layers x 7 linears, M = 2048, every NF4 weight resident).  A step is the forward
+    over all linears, layer 0 first, then the backward in reverse order, each linear on
+    its own seeded inputs; FLOPs 4 M in out + 6 M r (in + out) per linear."""
+    cfg = workloads.CONFIGS[cfg_idx]
+    lins = cfg.linears
+    L = cfg.layers
+    M, r = lins[0].M, lins[0].r
+
+    if cfg_idx == 5:
+        tensor = workloads.stack_tensor
+        xslot = workloads.STACK_INPUT_SLOT
+    else:
+        def tensor(layer, j, what):
+            lin = lins[j]
+            sd = lambda tid: workloads.seed_for(cfg_idx, 10 * layer + j, tid)
+            shape = {"W": (lin.d_out, lin.d_in), "A": (lin.d_in, r), "B": (r, lin.d_out),
+                     "X": (M, lin.d_in), "dY": (M, lin.d_out)}[what]
+            tid = {"W": workloads.TID_W, "A": workloads.TID_A, "B": workloads.TID_B,
+                   "X": workloads.TID_X, "dY": workloads.TID_DY}[what]
+            std = 0.02 if what in ("W", "A", "B") else 1.0
+            op = lin.outlier_p if what == "W" else 0.0
+            return workloads.device_normal_bf16(sd(tid), shape, std, dev, outlier_p=op,
+                                                mask_seed=sd(workloads.TID_MASK))
+        xslot = tuple(range(len(lins)))
+
+    ws = torch.empty(max(max(Q.qlora_quantize_workspace(l.d_out, l.d_in), Q.qlora_fwd_workspace(M, l.d_in, l.d_out, r),
+                             Q.qlora_bwd_workspace(M, l.d_in, l.d_out, r)) for l in lins),
+                     dtype=torch.uint8, device=dev)
+    wq = [[Q.nf4_alloc(l.d_out, l.d_in, True, dev) for l in lins] for _ in range(L)]
+    quant_us = 0.0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for layer in range(L):
+        for j in range(len(lins)):
+            W = tensor(layer, j, "W")
+            e0.record()
+            Q.qlora_quantize_nf4(W, True, out=wq[layer][j], workspace=ws)
+            e1.record()
+            torch.cuda.synchronize()
+            quant_us += 1e3 * e0.elapsed_time(e1)
+            del W
+    AB = [[(tensor(layer, j, "A"), tensor(layer, j, "B")) for j in range(len(lins))] for layer in range(L)]
+    X = [{j: tensor(layer, j, "X") for j in sorted(set(xslot))} for layer in range(L)]
+    dY = [[tensor(layer, j, "dY") for j in range(len(lins))] for layer in range(L)]
+    T = [[torch.empty((M, r), dtype=torch.bfloat16, device=dev) for _ in lins] for _ in range(L)]
+    Y = [torch.empty((M, l.d_out), dtype=torch.bfloat16, device=dev) for l in lins]
+    dX = [torch.empty((M, l.d_in), dtype=torch.bfloat16, device=dev) for l in lins]
+    dA = [[torch.empty((l.d_in, r), dtype=torch.float32, device=dev) for l in lins] for _ in range(L)]
+    dB = [[torch.empty((r, l.d_out), dtype=torch.float32, device=dev) for l in lins] for _ in range(L)]
+    torch.cuda.synchronize()
+
+    def step():
+        for layer in range(L):
+            for j, l in enumerate(lins):
+                A, B = AB[layer][j]
+                Q.qlora_linear_fwd(X[layer][xslot[j]], wq[layer][j], A, B, l.scale, Y=Y[j], T_save=T[layer][j],
+                                   workspace=ws)
+        for layer in reversed(range(L)):
+            for j, l in enumerate(lins):
+                A, B = AB[layer][j]
+                Q.qlora_linear_bwd(dY[layer][j], X[layer][xslot[j]], T[layer][j], wq[layer][j], A, B, l.scale,
+                                   dX=dX[j], dA=dA[layer][j], dB=dB[layer][j], workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = L * sum(flops_fwd_bwd(M, l.d_in, l.d_out, r) for l in lins)
+    Q.qlora_profile_enable(True)
+    Q.qlora_profile_read(reset=True)
+    step()
+    torch.cuda.synchronize()
+    prof = Q.qlora_profile_read(reset=True)
+    Q.qlora_profile_enable(False)
+    nf4_bytes = sum(w.nbytes() for row in wq for w in row)
+    out = {"workload": cfg.name, "layers": L, "linears": L * len(lins), "steps": steps, "warmup": warmup,
+           "ms_per_step": ms, "flops_per_step": flops, "TFLOPs": flops / (ms * 1e-3) / 1e12,
+           "frac": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "peak": PEAK_BF16_TFLOPS,
+           "nf4_resident_GB": nf4_bytes / 1e9, "hbm_allocated_GB": torch.cuda.memory_allocated() / 1e9,
+           "quantize_all_ms": quant_us / 1e3,
+           "kernels_ms_per_step": {k: t for k, (n, t) in prof.items()}}
+    del wq, AB, X, dY, T, Y, dX, dA, dB, ws
+    torch.cuda.empty_cache()
     return out
 
 

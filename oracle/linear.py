@@ -59,6 +59,14 @@ def backward_dx_rows(dY, Wq, A, B, s: float, rows):
     return dy @ w + s * ((dy @ b.T) @ a.T)
 
 
+def adapter_grads(dY, X, A, B, s: float):
+    """(dA [in][r], dB [r][out]) in float64: the backward's adapter gradients alone,
+    for full-size checks where the frozen-weight term of dX is sampled separately."""
+    dy, x, a, b = _f64(dY), _f64(X), _f64(A), _f64(B)
+    g = dy @ b.T
+    return s * (x.T @ g), s * ((x @ a).T @ dy)
+
+
 def flops_fwd(M, d_in, d_out, r) -> int:
     return 2 * M * d_in * d_out + 2 * M * r * (d_in + d_out)
 

@@ -35,6 +35,19 @@ def test_backward_matches_autograd(s):
     np.testing.assert_allclose(dx, X.grad.numpy(), rtol=1e-11, atol=1e-11)
     np.testing.assert_allclose(da, A.grad.numpy(), rtol=1e-11, atol=1e-11)
     np.testing.assert_allclose(db, B.grad.numpy(), rtol=1e-11, atol=1e-11)
+    # the adapter-only gradients used by the sampled full-size checks, and the slicing
+    # they rely on: Y's columns come from the weight's rows (and B's columns), dX's
+    # columns from the weight's columns (and A's rows)
+    da2, db2 = linear.adapter_grads(inp.dY, inp.X, inp.A, inp.B, s)
+    np.testing.assert_allclose(da2, A.grad.numpy(), rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(db2, B.grad.numpy(), rtol=1e-11, atol=1e-11)
+    cols = np.array([0, 5, 77, 191])
+    yc, _ = linear.forward(inp.X, Wd[cols], inp.A, inp.B[:, cols], s)
+    np.testing.assert_allclose(yc, Y.detach().numpy()[:, cols], rtol=1e-12, atol=1e-12)
+    kc = np.array([1, 64, 127])
+    rows = np.arange(12)
+    dxc = linear.backward_dx_rows(inp.dY, Wd[:, kc], inp.A[kc], inp.B, s, rows)
+    np.testing.assert_allclose(dxc, X.grad.numpy()[:, kc], rtol=1e-11, atol=1e-11)
 
 
 def test_frozen_weight_gets_no_gradient_and_dX_passes_through_W():

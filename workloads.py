@@ -130,15 +130,54 @@ def linear_inputs(cfg: int, lin: Linear, layer: int = 0, which=("W", "A", "B", "
     return LinearInputs(out.get("W"), out.get("A"), out.get("B"), out.get("X"), out.get("dY"), lin)
 
 
-def device_normal_bf16(seed: int, shape, std: float, device="cuda"):
-    """N(0, std^2) drawn on the device with torch's Philox generator, rounded once to bf16."""
+def device_normal_bf16(seed: int, shape, std: float, device="cuda", outlier_p: float = 0.0,
+                       outlier_scale: float = 20.0, mask_seed: int | None = None):
+    """N(0, std^2) drawn on the device with torch's Philox generator, optional outliers
+    (a Bernoulli(outlier_p) mask scales the fp32 entries), rounded once to bf16."""
     import torch
 
     g = torch.Generator(device=device)
     g.manual_seed(seed)
     x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
     x.mul_(std)
+    if outlier_p > 0.0:
+        g.manual_seed(mask_seed if mask_seed is not None else seed + 5)
+        mask = torch.rand(shape, generator=g, device=device, dtype=torch.float32) < outlier_p
+        x[mask] *= outlier_scale
+        del mask
     return x.to(torch.bfloat16)
+
+
+# The 65B layer stack (configuration 5).  Every linear of every layer has its own
+# weight, adapter factors and output gradient.  There is no attention or MLP
+# nonlinearity on the path, so the token inputs follow the layer's wiring only: q, k,
+# v, gate and up read one shared [M][8192] input (drawn with slot 0's seed), o reads
+# its own [M][8192] input (slot 3) and down its own [M][22016] input (slot 6).
+# Seeds: seed_for(5, 7*layer + slot, tensor_id), i.e. each linear of the stack counts
+# as one "layer" of the general seed rule.
+STACK_INPUT_SLOT = (0, 0, 0, 3, 0, 0, 6)
+
+
+def stack_seed(layer: int, slot: int, tensor_id: int) -> int:
+    return seed_for(5, 7 * layer + slot, tensor_id)
+
+
+def stack_tensor(layer: int, slot: int, what: str, device="cuda"):
+    """One device tensor of the 65B stack: "W" [out][in], "A" [in][r], "B" [r][out],
+    "X" (the input this linear reads) [M][in], "dY" [M][out]; bf16, torch Philox."""
+    lin = CONFIGS[5].linears[slot]
+    if what == "W":
+        return device_normal_bf16(stack_seed(layer, slot, TID_W), (lin.d_out, lin.d_in), 0.02, device)
+    if what == "A":
+        return device_normal_bf16(stack_seed(layer, slot, TID_A), (lin.d_in, lin.r), 0.02, device)
+    if what == "B":
+        return device_normal_bf16(stack_seed(layer, slot, TID_B), (lin.r, lin.d_out), 0.02, device)
+    if what == "X":
+        src = STACK_INPUT_SLOT[slot]
+        return device_normal_bf16(stack_seed(layer, src, TID_X), (lin.M, lin.d_in), 1.0, device)
+    if what == "dY":
+        return device_normal_bf16(stack_seed(layer, slot, TID_DY), (lin.M, lin.d_out), 1.0, device)
+    raise ValueError(what)
 
 
 def custom_linear(M: int, d_in: int, d_out: int, r: int, seed: int, alpha: float = 16.0,
