@@ -83,12 +83,12 @@ hipError_t launch_fwd_gemm(const uint16_t* X, int64_t M, int64_t K, int64_t N, c
 // slices of ka rows); launch_gemv_epilogue forms T, Ts = bf16(s T), T_save = bf16(T) when
 // T_save is not NULL, and Y = bf16( sum of weight partials + Ts B ).
 struct GemvPlan {
-  int splits;
-  int64_t kb_per_split;
-  int64_t wgroups, agroups;   // 64-row weight groups, 64-column adapter groups
-  int64_t npad;               // weight partial row length (wgroups * 64)
-  int64_t ka;                 // rows of A per adapter slice
-  int asplits;
+  int splits;                 // weight slices of 32 blocks (2048 reduction indices)
+  int64_t rgroups;            // 16-row groups of the weight
+  int64_t rranges;            // weight workgroups per slice (contiguous ranges of row groups)
+  int64_t npad;               // weight partial row length (rgroups * 16)
+  int64_t agroups;            // 64-column adapter groups
+  int asplits;                // adapter slices of 2048 rows of A
   size_t tpart;               // float offset of the adapter partials
 };
 GemvPlan gemv_plan(int64_t M, int64_t K, int64_t N, int64_t rp);

@@ -85,6 +85,14 @@ def test_options_no_double_quant_recompute_T_skip_dX():
     _check_full(inp, need_dX=False, label="no-dX")
 
 
+@pytest.mark.parametrize("dq", [True, False])
+def test_skinny_ragged_reduction_and_rows(dq):
+    """Skinny path with a reduction of 5 blocks (one weight slice, most of its waves past
+    the end) and 40 output rows (a partial 16-row group), with and without double quant."""
+    inp = workloads.custom_linear(3, 320, 40, 8, seed=11)
+    _check_full(inp, dq=dq, label=f"skinny-ragged dq={dq}")
+
+
 def test_empty_token_batch():
     require_gpu()
     inp = workloads.custom_linear(1, 256, 128, 8, seed=4)
