@@ -21,6 +21,8 @@ Also reported:
                   rotating 6 weight copies (> 512 MB) per shape;
   quantize     -- quantize + double-quantize of the headline weight (timed apart):
                   bytes moved (bf16 in, codes and constants out) over time;
+  formats      -- quantization error (relative MSE of the dequantized weight) of the
+                  NF4, FP4 and Int4 tables on the headline weight shape;
   mlp_7b, stack_65b -- forward+backward TFLOP/s over the 7B MLP pair (M = 4096)
                   and over the 65B layer stack (80 layers x 7 linears, M = 2048,
                   all 33 GB of NF4 weight resident), forward layer 0 first, then
@@ -238,6 +240,9 @@ def main():
     if args.only in ("all", "gemv") and not args.no_gemv:
         result["gemv"] = bench_gemv(Q, workloads, torch, dev, args.gemv_iters)
 
+    if args.only in ("all", "headline"):
+        result["formats"] = bench_formats(Q, workloads, torch, dev)
+
     if args.only in ("all", "layers") and not args.no_layers:
         result["mlp_7b"] = bench_layers(Q, workloads, torch, dev, 3, args.layer_steps, 1)
         result["stack_65b"] = bench_layers(Q, workloads, torch, dev, 5, args.layer_steps, 1)
@@ -388,6 +393,24 @@ def bench_layers(Q, workloads, torch, dev, cfg_idx, steps, warmup):
            "quantize_all_ms": quant_us / 1e3,
            "kernels_ms_per_step": {k: t for k, (n, t) in prof.items()}}
     del wq, AB, X, dY, T, Y, dX, dA, dB, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_formats(Q, workloads, torch, dev):
+    """Quantization error of the three 16-entry tables (NF4, FP4 = E2M1 / 6, Int4 = k / 7)
+    on the headline weight shape, with double quantization: relative mean squared error of
+    the dequantized bf16 weight, the synthetic stand-in for the pages' data-type comparison."""
+    W = workloads.device_normal_bf16(2500, (4096, 4096), 0.02)
+    w = W.float()
+    den = (w * w).mean().item()
+    out = {}
+    for name, cb in Q.CODEBOOKS.items():
+        q = Q.qlora_quantize_nf4(W, True, codebook=cb)
+        d = Q.qlora_dequant(q).float()
+        out[name] = {"rel_mse": ((d - w) ** 2).mean().item() / den}
+        del q, d
+    out["order"] = " < ".join(sorted(Q.CODEBOOKS, key=lambda k: out[k]["rel_mse"]))
     torch.cuda.empty_cache()
     return out
 

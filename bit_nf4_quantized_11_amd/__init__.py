@@ -15,7 +15,8 @@ import torch
 from . import _lib
 
 __all__ = [
-    "NF4Weight", "QLoRAError", "nf4_alloc", "qlora_nf4_codebook", "qlora_nf4_sizes", "qlora_quantize_workspace",
+    "NF4Weight", "QLoRAError", "nf4_alloc", "qlora_nf4_codebook", "qlora_codebook_table", "qlora_nf4_sizes",
+    "CODEBOOK_NF4", "CODEBOOK_FP4", "CODEBOOK_INT4", "CODEBOOKS", "qlora_quantize_workspace",
     "qlora_fwd_workspace", "qlora_bwd_workspace", "qlora_quantize_nf4", "qlora_dequant", "qlora_linear_fwd",
     "qlora_linear_bwd", "qlora_profile_enable", "qlora_profile_read", "lib",
 ]
@@ -23,6 +24,11 @@ __all__ = [
 
 class QLoRAError(RuntimeError):
     pass
+
+
+# qlora_codebook values: the 16-entry table a quantized weight's codes index
+CODEBOOK_NF4, CODEBOOK_FP4, CODEBOOK_INT4 = 0, 1, 2
+CODEBOOKS = {"nf4": CODEBOOK_NF4, "fp4": CODEBOOK_FP4, "int4": CODEBOOK_INT4}
 
 
 def lib():
@@ -61,9 +67,10 @@ class NF4Weight:
     absmax: torch.Tensor     # uint8 [nblk] (double quant) or float32 [nblk]
     c1: torch.Tensor | None  # float32 [nsup]
     mu: torch.Tensor | None  # float32 [1]
+    codebook: int = CODEBOOK_NF4
 
     def desc(self) -> _lib.qlora_nf4:
-        return _lib.qlora_nf4(self.rows, self.cols, int(self.double_quant), 0, self.codes.data_ptr(),
+        return _lib.qlora_nf4(self.rows, self.cols, int(self.double_quant), int(self.codebook), self.codes.data_ptr(),
                               self.absmax.data_ptr(), self.c1.data_ptr() if self.c1 is not None else None,
                               self.mu.data_ptr() if self.mu is not None else None)
 
@@ -76,6 +83,14 @@ def qlora_nf4_codebook():
     lv = (C.c_float * 16)()
     th = (C.c_float * 15)()
     _check(lib().qlora_nf4_codebook(lv, th), "qlora_nf4_codebook")
+    return list(lv), list(th)
+
+
+def qlora_codebook_table(codebook: int = CODEBOOK_NF4):
+    """(levels[16], thresholds[15]) of any codebook, computed by the library."""
+    lv = (C.c_float * 16)()
+    th = (C.c_float * 15)()
+    _check(lib().qlora_codebook_table(int(codebook), lv, th), "qlora_codebook_table")
     return list(lv), list(th)
 
 
@@ -105,7 +120,7 @@ def _workspace(nbytes: int, device, ws):
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
-def nf4_alloc(rows: int, cols: int, double_quant: bool = True, device="cuda") -> NF4Weight:
+def nf4_alloc(rows: int, cols: int, double_quant: bool = True, device="cuda", codebook: int = CODEBOOK_NF4) -> NF4Weight:
     cb, ab, c1b, mub = qlora_nf4_sizes(rows, cols, double_quant)
     codes = torch.empty(cb, dtype=torch.uint8, device=device)
     if double_quant:
@@ -115,16 +130,18 @@ def nf4_alloc(rows: int, cols: int, double_quant: bool = True, device="cuda") ->
     else:
         absmax = torch.empty(ab // 4, dtype=torch.float32, device=device)
         c1 = mu = None
-    return NF4Weight(rows, cols, double_quant, codes, absmax, c1, mu)
+    return NF4Weight(rows, cols, double_quant, codes, absmax, c1, mu, codebook)
 
 
 def qlora_quantize_nf4(W: torch.Tensor, double_quant: bool = True, out: NF4Weight | None = None,
-                       workspace: torch.Tensor | None = None, stream=None) -> NF4Weight:
-    """Quantize a bf16 [rows][cols] weight (any 2-D shape) to NF4 (+ double quantization)."""
+                       workspace: torch.Tensor | None = None, stream=None, codebook: int = CODEBOOK_NF4) -> NF4Weight:
+    """Quantize a bf16 [rows][cols] weight (any 2-D shape) to 4-bit codes of `codebook`
+    (NF4 by default) with blockwise absmax (+ double quantization).  With `out` given,
+    its own codebook is used."""
     _bf16(W, "W")
     rows, cols = (W.shape[0], W.shape[1]) if W.dim() == 2 else (1, W.numel())
     if out is None:
-        out = nf4_alloc(rows, cols, double_quant, W.device)
+        out = nf4_alloc(rows, cols, double_quant, W.device, codebook)
     ws = _workspace(qlora_quantize_workspace(rows, cols, out.double_quant), W.device, workspace)
     d = out.desc()
     _check(lib().qlora_quantize_nf4(_ptr(W), rows, cols, C.byref(d), _ptr(ws),

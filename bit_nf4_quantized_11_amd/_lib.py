@@ -23,7 +23,7 @@ class qlora_nf4(C.Structure):
         ("rows", C.c_int64),
         ("cols", C.c_int64),
         ("double_quant", C.c_int32),
-        ("reserved", C.c_int32),
+        ("codebook", C.c_int32),
         ("codes", C.c_void_p),
         ("absmax", C.c_void_p),
         ("c1", C.c_void_p),
@@ -40,6 +40,7 @@ SIGNATURES = {
     "qlora_status_str": (C.c_char_p, [C.c_int]),
     "qlora_version": (C.c_char_p, []),
     "qlora_nf4_codebook": (C.c_int, [C.POINTER(C.c_float), C.POINTER(C.c_float)]),
+    "qlora_codebook_table": (C.c_int, [C.c_int32, C.POINTER(C.c_float), C.POINTER(C.c_float)]),
     "qlora_nf4_sizes": (C.c_int, [C.c_int64, C.c_int64, C.c_int32, C.POINTER(C.c_size_t), C.POINTER(C.c_size_t),
                                   C.POINTER(C.c_size_t), C.POINTER(C.c_size_t)]),
     "qlora_quantize_workspace": (C.c_size_t, [C.c_int64, C.c_int64, C.c_int32]),

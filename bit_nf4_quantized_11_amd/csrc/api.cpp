@@ -93,6 +93,7 @@ NF4View view_of(const qlora_nf4* w) {
   v.c1 = w->c1;
   v.mu = w->mu;
   v.dq = w->double_quant;
+  v.cb = w->codebook;
   return v;
 }
 
@@ -104,6 +105,7 @@ NF4View view_of(const qlora_nf4* w) {
 qlora_status check_nf4(const qlora_nf4* w) {
   if (!w || !w->codes || !w->absmax) return QLORA_ERR_NULL;
   if (w->double_quant != 0 && w->double_quant != 1) return QLORA_ERR_UNSUPPORTED;
+  if (w->codebook < 0 || w->codebook >= kNumCodebooks) return QLORA_ERR_UNSUPPORTED;
   if (w->double_quant && (!w->c1 || !w->mu)) return QLORA_ERR_NULL;
   if (w->rows < 1 || w->cols < 1 || w->rows >= kMaxDim || w->cols >= kMaxDim) return QLORA_ERR_SHAPE;
   if (!aligned16(w->codes) || !aligned4(w->absmax) || (w->c1 && !aligned4(w->c1)) || (w->mu && !aligned4(w->mu)))
@@ -232,6 +234,13 @@ const char* qlora_status_str(qlora_status s) {
 
 const char* qlora_version(void) { return "libqlora 0.1 (gfx950)"; }
 
+qlora_status qlora_codebook_table(int32_t codebook, float levels[16], float thresholds[15]) {
+  if (codebook < 0 || codebook >= kNumCodebooks) return QLORA_ERR_UNSUPPORTED;
+  if (levels) std::memcpy(levels, codebook_levels_host(codebook), 16 * sizeof(float));
+  if (thresholds) std::memcpy(thresholds, codebook_thresholds_host(codebook), 15 * sizeof(float));
+  return QLORA_OK;
+}
+
 qlora_status qlora_nf4_codebook(float levels[16], float thresholds[15]) {
   if (levels) std::memcpy(levels, nf4_levels_host(), 16 * sizeof(float));
   if (thresholds) std::memcpy(thresholds, nf4_thresholds_host(), 15 * sizeof(float));
@@ -283,11 +292,11 @@ qlora_status qlora_quantize_nf4(const uint16_t* W, int64_t rows, int64_t cols, c
     if (!aligned16(ws)) return QLORA_ERR_ALIGN;
     const QuantWs q = quant_layout(ws, numel);
     QL_HIP(launch_fill_u32(reinterpret_cast<uint32_t*>(q.hist), 512 * kHistCopies, 0u, stream));
-    QL_HIP(launch_quantize(W, numel, out->codes, q.absmax, q.hist, stream));
+    QL_HIP(launch_quantize(W, numel, out->codebook, out->codes, q.absmax, q.hist, stream));
     QL_HIP(launch_dq_mean(q.hist, nblk, out->mu, stream));
     QL_HIP(launch_dq_encode(q.absmax, nblk, out->mu, static_cast<uint8_t*>(out->absmax), out->c1, stream));
   } else {
-    QL_HIP(launch_quantize(W, numel, out->codes, static_cast<float*>(out->absmax), nullptr, stream));
+    QL_HIP(launch_quantize(W, numel, out->codebook, out->codes, static_cast<float*>(out->absmax), nullptr, stream));
   }
   return QLORA_OK;
 }

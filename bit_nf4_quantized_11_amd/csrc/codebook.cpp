@@ -1,4 +1,5 @@
-// Host computation of the NF4 levels and encoder thresholds.
+// Host computation of the codebooks' levels and encoder thresholds: NF4, and the
+// FP4 (E2M1) and Int4 tables the pages compare it with.
 //
 // Procedure ("QLoRA: Efficient Finetuning of Quantized LLMs", section
 // "NormalFloat: 4 bits for a bell curve", the code-point listing): take
@@ -51,7 +52,37 @@ float round_down_f32(double v) {
 struct Codebook {
   float level[16];
   float thr[15];
-  Codebook() {
+  void finish(const double* v) {
+    for (int i = 0; i < 16; ++i) level[i] = (float)v[i];
+    for (int k = 0; k < 15; ++k) thr[k] = round_down_f32(((double)level[k] + (double)level[k + 1]) * 0.5);
+  }
+  // 4-bit float, 2 exponent bits (bias 1) and 1 mantissa bit: magnitudes m/2 (exponent 0)
+  // and 2^(e-1) (1 + m/2), i.e. 0, 0.5, 1, 1.5, 2, 3, 4, 6; divided by the largest (6).
+  // Index 0 is the unused entry -4/3 (the next E2M1-like step beyond the range).
+  static Codebook fp4() {
+    double mag[8];
+    for (int c = 0; c < 8; ++c) {
+      const int e = c >> 1, m = c & 1;
+      mag[c] = e == 0 ? 0.5 * m : std::ldexp(1.0 + 0.5 * m, e - 1);
+    }
+    double v[16];
+    v[0] = -8.0 / 6.0;
+    for (int i = 0; i < 7; ++i) v[1 + i] = -mag[7 - i] / 6.0;   // -1 .. -1/12
+    for (int i = 0; i < 8; ++i) v[8 + i] = mag[i] / 6.0;        // 0 .. 1
+    Codebook cb;
+    cb.finish(v);
+    return cb;
+  }
+  // symmetric int4: k / 7, k = -8..7; index 0 (-8/7) is never the nearest level in [-1, 1]
+  static Codebook int4() {
+    double v[16];
+    for (int i = 0; i < 16; ++i) v[i] = (double)(i - 8) / 7.0;
+    Codebook cb;
+    cb.finish(v);
+    return cb;
+  }
+  Codebook() = default;
+  static Codebook nf4() {
     double v[16];
     int n = 0;
     const double step_pos = (0.5 - kOffset) / 8.0;   // 9 points, last (1/2) dropped
@@ -68,20 +99,27 @@ struct Codebook {
     }
     double mx = 0.0;
     for (int i = 0; i < 16; ++i) mx = std::fmax(mx, std::fabs(v[i]));
-    for (int i = 0; i < 16; ++i) level[i] = (float)(v[i] / mx);
-    for (int k = 0; k < 15; ++k) thr[k] = round_down_f32(((double)level[k] + (double)level[k + 1]) * 0.5);
+    for (int i = 0; i < 16; ++i) v[i] = v[i] / mx;
+    Codebook cb;
+    cb.finish(v);
+    return cb;
   }
 };
 
 }  // namespace
 
-static const Codebook& codebook() {
-  static const Codebook cb;   // computed once; thread-safe initialization
-  return cb;
+static const Codebook& codebook(int which) {
+  // computed once; thread-safe initialization
+  static const Codebook tables[3] = {Codebook::nf4(), Codebook::fp4(), Codebook::int4()};
+  return tables[which];
 }
 
-const float* nf4_levels_host() { return codebook().level; }
+const float* codebook_levels_host(int which) { return codebook(which).level; }
 
-const float* nf4_thresholds_host() { return codebook().thr; }
+const float* codebook_thresholds_host(int which) { return codebook(which).thr; }
+
+const float* nf4_levels_host() { return codebook(0).level; }
+
+const float* nf4_thresholds_host() { return codebook(0).thr; }
 
 }  // namespace qlora

@@ -35,6 +35,7 @@ struct NF4View {
   const float* c1;
   const float* mu;
   int32_t dq;
+  int32_t cb;             // codebook: index of the 16-entry table the codes refer to
 };
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

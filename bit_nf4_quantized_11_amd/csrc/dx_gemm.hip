@@ -176,7 +176,7 @@ hipError_t launch_dx_gemm(const uint16_t* dY, int64_t M, int64_t K, int64_t N, c
                           hipStream_t s) {
   const uint64_t nblk = (uint64_t)N * K / 64;
   DxParams p{dY, M, K, N, w, nblk * kBlockBytes, w.dq ? nblk : nblk * 4, w.dq ? ((nblk + 255) / 256) * 4 : 0,
-             Gs, rp, A, r, dX, nf4_table()};
+             Gs, rp, A, r, dX, nf4_table(w.cb)};
   const int64_t tiles = ((M + BT - 1) / BT) * ((K + BF - 1) / BF);
   ProfScope ps("k_bwd_dx_nf4_gemm", s);
   const dim3 grid((unsigned)tiles), block(NT);

@@ -172,7 +172,7 @@ hipError_t launch_fwd_gemm(const uint16_t* X, int64_t M, int64_t K, int64_t N, c
                            hipStream_t s) {
   const uint64_t nblk = (uint64_t)N * K / 64;
   FwdParams p{X, M, K, N, w, nblk * kBlockBytes, w.dq ? nblk : nblk * 4, w.dq ? ((nblk + 255) / 256) * 4 : 0,
-              Ts, rp, B, r, Y, nf4_table()};
+              Ts, rp, B, r, Y, nf4_table(w.cb)};
   const int64_t tiles = ((M + BT - 1) / BT) * ((N + BF - 1) / BF);
   ProfScope ps("k_fwd_nf4_gemm", s);
   if (w.dq)

@@ -427,7 +427,7 @@ hipError_t launch_gemv(const uint16_t* X, int64_t M, int64_t K, int64_t N, const
   const uint64_t nblk = (uint64_t)N * K / 64;
   GemvParams p{X, M, K, N, w, nblk * kBlockBytes, w.dq ? nblk : nblk * 4, w.dq ? ((nblk + 255) / 256) * 4 : 0,
                A, r, partial, partial + pl.tpart, pl.npad, pl.agroups * GROWS, pl.splits, pl.rgroups,
-               pl.rranges, pl.agroups, pl.asplits, nf4_table()};
+               pl.rranges, pl.agroups, pl.asplits, nf4_table(w.cb)};
   const size_t lds = std::max(kLdsWeight, kLdsAdapter);
   ProfScope ps("k_fwd_nf4_gemv", s);
   const dim3 grid((unsigned)(pl.rranges * pl.splits + pl.agroups * pl.asplits));

@@ -13,7 +13,10 @@ namespace qlora {
 // Host-side NF4 table (computed once, see codebook.cpp).
 const float* nf4_levels_host();
 const float* nf4_thresholds_host();
-NF4Table nf4_table();
+constexpr int kNumCodebooks = 3;   // NF4, FP4, INT4
+const float* codebook_levels_host(int which);
+const float* codebook_thresholds_host(int which);
+NF4Table nf4_table(int which);
 
 // Optional per-launch timing (api.cpp).
 struct ProfScope {
@@ -25,7 +28,7 @@ struct ProfScope {
 
 // ---- quantize / dequantize (quant.hip) --------------------------------------------------
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
-hipError_t launch_quantize(const uint16_t* W, int64_t numel, uint8_t* codes, float* absmax_f32,
+hipError_t launch_quantize(const uint16_t* W, int64_t numel, int codebook, uint8_t* codes, float* absmax_f32,
                            unsigned long long* hist, hipStream_t s);
 hipError_t launch_dq_mean(const unsigned long long* hist, int64_t nblk, float* mu, hipStream_t s);
 hipError_t launch_dq_encode(const float* absmax_f32, int64_t nblk, const float* mu, uint8_t* c2, float* c1,

@@ -246,10 +246,10 @@ inline unsigned grid_for(int64_t work, int64_t per_block, unsigned cap) {
 
 }  // namespace
 
-NF4Table nf4_table() {
+NF4Table nf4_table(int which) {
   NF4Table t;
-  const float* l = nf4_levels_host();
-  const float* th = nf4_thresholds_host();
+  const float* l = codebook_levels_host(which);
+  const float* th = codebook_thresholds_host(which);
   for (int i = 0; i < 16; ++i) t.level[i] = l[i];
   for (int i = 0; i < 15; ++i) t.thr[i] = th[i];
   t.pad_ = 0.0f;
@@ -263,12 +263,12 @@ hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_quantize(const uint16_t* W, int64_t numel, uint8_t* codes, float* absmax_f32,
+hipError_t launch_quantize(const uint16_t* W, int64_t numel, int codebook, uint8_t* codes, float* absmax_f32,
                            unsigned long long* hist, hipStream_t s) {
   const int64_t nblk = (numel + 63) / 64;
   ProfScope ps("k_nf4_quantize", s);
   hipLaunchKernelGGL(k_nf4_quantize, dim3(grid_for(nblk, kThreads / 8, 2048)), dim3(kThreads), 0, s, W, numel,
-                     codes, absmax_f32, hist, nf4_table());
+                     codes, absmax_f32, hist, nf4_table(codebook));
   return hipGetLastError();
 }
 
@@ -290,7 +290,7 @@ hipError_t launch_dequant(const NF4View& w, int64_t numel, uint16_t* out, hipStr
   const int64_t ngroups = (numel + 7) / 8;
   ProfScope ps("k_nf4_dequant", s);
   hipLaunchKernelGGL(k_nf4_dequant, dim3(grid_for(ngroups, kThreads, 16384)), dim3(kThreads), 0, s, w, numel, out,
-                     nf4_table());
+                     nf4_table(w.cb));
   return hipGetLastError();
 }
 

@@ -56,7 +56,8 @@ typedef enum {
  *            of 64, each stored whole in 32 bytes; inside a block the group of 8
  *            elements 8g..8g+7 sits in bytes 4g..4g+3, and byte i of a group holds
  *            element i in bits 3..0 and element i+4 in bits 7..4.  Positions past
- *            the end of the tensor hold code 7 (the exact zero).
+ *            the end of the tensor hold the code of the table's exact zero (7 for
+ *            NF4, 8 for FP4 and INT4).
  *   absmax : double_quant = 1 -> nblk bytes, FP8 E4M3 code of (absmax_b - mu) / c1
  *            double_quant = 0 -> nblk floats, the block absmax itself
  *            (nblk = ceil(rows*cols / 64))
@@ -72,7 +73,7 @@ typedef struct {
   int64_t rows;
   int64_t cols;
   int32_t double_quant;
-  int32_t reserved;
+  int32_t codebook;      /* qlora_codebook: the 16-entry table the codes index (0 = NF4) */
   uint8_t* codes;
   void* absmax;
   float* c1;
@@ -96,6 +97,25 @@ const char* qlora_version(void);
  * Either pointer may be NULL.                                                   */
 qlora_status qlora_nf4_codebook(float levels[16], float thresholds[15]);
 
+/* The 16-entry tables a quantized weight can use (qlora_nf4.codebook).  Every table
+ * is strictly ascending, spans [-1, 1] with an exact zero, and is used the same way
+ * (encoder thresholds at the rounded-down midpoints, dequant level[code] * s').
+ *   QLORA_CODEBOOK_NF4  -- the NormalFloat levels above (zero at index 7).
+ *   QLORA_CODEBOOK_FP4  -- the 15 values of a 4-bit float with 2 exponent and 1
+ *                          mantissa bits (OCP E2M1: 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their
+ *                          negatives) divided by 6, so the block maximum maps to 1;
+ *                          index 0 holds -4/3, outside [-1, 1], never chosen (E2M1's two
+ *                          zeros leave one of its 16 codes without a value of its own).
+ *   QLORA_CODEBOOK_INT4 -- k / 7 for k = -8..7 (symmetric absmax int4, round(7 x));
+ *                          index 0 (-8/7) is never chosen.
+ * The pages compare NF4 with FP4 and Int4 data types ("NormalFloat: 4 bits for a
+ * bell curve"); they print no FP4 table, so this one is E2M1, stated here.       */
+typedef enum { QLORA_CODEBOOK_NF4 = 0, QLORA_CODEBOOK_FP4 = 1, QLORA_CODEBOOK_INT4 = 2 } qlora_codebook;
+
+/* Host only.  Levels and encoder thresholds of any codebook (as qlora_nf4_codebook);
+ * UNSUPPORTED for an unknown codebook.  Either pointer may be NULL.               */
+qlora_status qlora_codebook_table(int32_t codebook, float levels[16], float thresholds[15]);
+
 /* Host only.  Bytes of each buffer of a quantized [rows][cols] weight
  * ("Double quantization": 4-bit codes, 8-bit constants per 64, one fp32 per
  * 256 constants, one fp32 mean).  rows, cols >= 1.  Any output may be NULL.   */
@@ -109,9 +129,9 @@ size_t qlora_bwd_workspace(int64_t M, int64_t in_features, int64_t out_features,
 
 /* Blockwise NF4 quantization of W [rows][cols] bf16 into `out` (whose rows,
  * cols, double_quant and buffers the caller sets; see qlora_nf4_sizes).
- * Per 64-block: a = max|w| (a below 2^-126 makes the block all code 7 with
- * a = 0); x = fl32(w * fl32(1/a)); code = nearest NF4 level, ties to the lower
- * index ("Quantize in blocks, not all at once"; "NormalFloat").  With
+ * Per 64-block: a = max|w| (a below 2^-126 makes the block all zero codes with
+ * a = 0); x = fl32(w * fl32(1/a)); code = nearest level of out->codebook, ties to
+ * the lower index ("Quantize in blocks, not all at once"; "NormalFloat").  With
  * double_quant: mu = fl32(S / nblk), S the exact sum of all a rounded once to
  * float64; per group of 256 blocks m = max|fl32(a - mu)|, c1 = fl32(m / 448)
  * (c1 below 2^-126 -> c1 = 0 and codes 0), c2 = E4M3_RNE(fl32(fl32(a - mu) *

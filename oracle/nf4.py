@@ -110,6 +110,57 @@ def nf4_levels(ppf=None) -> np.ndarray:
 # ----------------------------------------------------------------------------------------------
 # First-level quantization: blockwise absmax + nearest NF4 level
 # ----------------------------------------------------------------------------------------------
+# ----------------------------------------------------------------------------------------------
+# The other 4-bit data types the pages compare NF4 with ([Explainer] "NormalFloat: 4 bits for
+# a bell curve": NF4 against FP4 and Int4).  Each is a strictly ascending table of 16 fp32
+# values spanning [-1, 1] with an exact zero, used exactly like the NF4 levels.
+#   FP4: a 4-bit float with 2 exponent bits (bias 1) and 1 mantissa bit (the OCP E2M1
+#        layout; the pages print no FP4 table, so this one is a stated choice): magnitudes
+#        m/2 for exponent 0 and 2^(e-1) * (1 + m/2) otherwise, i.e. 0, 0.5, 1, 1.5, 2, 3,
+#        4, 6, with both signs, divided by 6 so the block maximum maps to 1.  Its +0 and -0
+#        coincide, which leaves 15 values; index 0 gets -4/3, outside [-1, 1], so it is
+#        never the nearest level and the table stays strictly ascending.
+#   Int4: k/7 for k = -8..7, the 4-bit version of the absmax integer quantizer
+#        round(127 x / absmax) of [Explainer] "Quantize in blocks, not all at once" with
+#        the largest code 7; k = -8 (index 0) is never the nearest level in [-1, 1].
+# ----------------------------------------------------------------------------------------------
+def e2m1_magnitude(code3: int) -> float:
+    """Magnitude of a 3-bit E2M1 pattern (2 exponent bits, bias 1, 1 mantissa bit)."""
+    e, m = code3 >> 1, code3 & 1
+    return 0.5 * m if e == 0 else 2.0 ** (e - 1) * (1.0 + 0.5 * m)
+
+
+def fp4_levels() -> np.ndarray:
+    mags = [e2m1_magnitude(c) for c in range(8)]               # 0, 0.5, ..., 6
+    vals = [-8.0 / 6.0] + [-v / 6.0 for v in reversed(mags[1:])] + [v / 6.0 for v in mags]
+    return np.array(vals, dtype=np.float64).astype(np.float32)
+
+
+def int4_levels() -> np.ndarray:
+    return (np.arange(-8, 8, dtype=np.float64) / 7.0).astype(np.float32)
+
+
+CODEBOOKS = ("nf4", "fp4", "int4")
+
+
+def codebook_levels(name: str = "nf4") -> np.ndarray:
+    """The 16 fp32 levels of a codebook: "nf4", "fp4" or "int4"."""
+    if name == "nf4":
+        return nf4_levels()
+    if name == "fp4":
+        return fp4_levels()
+    if name == "int4":
+        return int4_levels()
+    raise ValueError(name)
+
+
+def zero_code(levels: np.ndarray) -> int:
+    """Index of the exact zero of a table (the code of zero blocks and padding)."""
+    idx = np.flatnonzero(np.asarray(levels, dtype=np.float32) == 0.0)
+    assert idx.size == 1
+    return int(idx[0])
+
+
 def num_blocks(numel: int) -> int:
     return -(-numel // BLOCK)
 
@@ -161,8 +212,10 @@ def normalize_blocks(blocks: np.ndarray, absmax: np.ndarray) -> np.ndarray:
     return x
 
 
-def nf4_codes(w_bits: np.ndarray, absmax: np.ndarray | None = None) -> np.ndarray:
-    """Unpacked 4-bit codes (one uint8 per element, padded to whole blocks)."""
+def nf4_codes(w_bits: np.ndarray, absmax: np.ndarray | None = None, levels: np.ndarray | None = None) -> np.ndarray:
+    """Unpacked 4-bit codes (one uint8 per element, padded to whole blocks); NF4 unless
+    another table is given."""
+    lv = nf4_levels() if levels is None else levels
     blocks = _blocks_f32(w_bits)
     if absmax is None:
         absmax = blockwise_absmax(w_bits)
@@ -170,13 +223,15 @@ def nf4_codes(w_bits: np.ndarray, absmax: np.ndarray | None = None) -> np.ndarra
     rows_per_chunk = max(1, _CHUNK // BLOCK)
     for s in range(0, blocks.shape[0], rows_per_chunk):
         x = normalize_blocks(blocks[s:s + rows_per_chunk], absmax[s:s + rows_per_chunk])
-        codes[s:s + rows_per_chunk] = nearest_level(x).reshape(x.shape)
-    codes[absmax == 0] = ZERO_CODE
+        codes[s:s + rows_per_chunk] = nearest_level(x, lv).reshape(x.shape)
+    codes[absmax == 0] = zero_code(lv)
     return codes.reshape(-1)
 
 
-def codes_for_blocks(w_bits: np.ndarray, absmax: np.ndarray, block_ids: np.ndarray) -> np.ndarray:
+def codes_for_blocks(w_bits: np.ndarray, absmax: np.ndarray, block_ids: np.ndarray,
+                     levels: np.ndarray | None = None) -> np.ndarray:
     """Unpacked codes [len(block_ids), 64] of selected blocks only (for sampled checks at full size)."""
+    lv = nf4_levels() if levels is None else levels
     flat = np.ravel(w_bits)
     block_ids = np.asarray(block_ids, dtype=np.int64)
     blocks = np.zeros((block_ids.size, BLOCK), dtype=np.float32)
@@ -184,15 +239,16 @@ def codes_for_blocks(w_bits: np.ndarray, absmax: np.ndarray, block_ids: np.ndarr
         seg = bf16_to_f32(flat[b * BLOCK:(b + 1) * BLOCK])
         blocks[i, : seg.size] = seg
     a = absmax[block_ids]
-    codes = nearest_level(normalize_blocks(blocks, a)).reshape(blocks.shape)
-    codes[a == 0] = ZERO_CODE
+    codes = nearest_level(normalize_blocks(blocks, a), lv).reshape(blocks.shape)
+    codes[a == 0] = zero_code(lv)
     return codes
 
 
-def pack_nibbles(codes: np.ndarray, numel: int) -> np.ndarray:
-    """Codes -> 32 bytes per 64-block in the layout of reading R6; returns nblk*32 bytes."""
+def pack_nibbles(codes: np.ndarray, numel: int, pad_code: int = ZERO_CODE) -> np.ndarray:
+    """Codes -> 32 bytes per 64-block in the layout of reading R6; returns nblk*32 bytes.
+    Positions past numel hold pad_code (the table's zero; 7 for NF4)."""
     nblk = num_blocks(numel)
-    c = np.full(nblk * BLOCK, ZERO_CODE, dtype=np.uint8)
+    c = np.full(nblk * BLOCK, pad_code, dtype=np.uint8)
     c[:numel] = np.ravel(codes)[:numel]
     g = c.reshape(-1, 8)                                   # one row per 8-element group
     return (g[:, 0:4] | (g[:, 4:8] << 4)).astype(np.uint8).reshape(-1)
@@ -287,13 +343,15 @@ def block_scales_dq(c2: np.ndarray, c1: np.ndarray, mu: np.float32) -> np.ndarra
 # ----------------------------------------------------------------------------------------------
 # Whole-tensor quantize / dequantize
 # ----------------------------------------------------------------------------------------------
-def quantize(w_bits: np.ndarray, double_quant: bool = True) -> dict:
-    """Quantize a bf16 weight (any shape; flattened row-major) to NF4 with optional double quant."""
+def quantize(w_bits: np.ndarray, double_quant: bool = True, codebook: str = "nf4") -> dict:
+    """Quantize a bf16 weight (any shape; flattened row-major) to 4-bit codes of a codebook
+    (NF4 by default) with optional double quant."""
     numel = int(np.asarray(w_bits).size)
+    lv = codebook_levels(codebook)
     absmax = blockwise_absmax(w_bits)
-    codes = nf4_codes(w_bits, absmax)
-    q = {"numel": numel, "codes": pack_nibbles(codes, numel), "absmax_true": absmax,
-         "double_quant": bool(double_quant)}
+    codes = nf4_codes(w_bits, absmax, lv)
+    q = {"numel": numel, "codes": pack_nibbles(codes, numel, zero_code(lv)), "absmax_true": absmax,
+         "double_quant": bool(double_quant), "codebook": codebook}
     if double_quant:
         c2, c1, mu = double_quantize(absmax)
         q.update(c2=c2, c1=c1, mu=mu, scales=block_scales_dq(c2, c1, mu))
@@ -302,9 +360,10 @@ def quantize(w_bits: np.ndarray, double_quant: bool = True) -> dict:
     return q
 
 
-def dequantize_codes(codes_unpacked: np.ndarray, scales: np.ndarray) -> np.ndarray:
-    """Outer dequant: bf16_RNE(fl32(level[code] * s')) per element (reading R12)."""
-    lv = nf4_levels()
+def dequantize_codes(codes_unpacked: np.ndarray, scales: np.ndarray, levels: np.ndarray | None = None) -> np.ndarray:
+    """Outer dequant: bf16_RNE(fl32(level[code] * s')) per element (reading R12); NF4
+    levels unless another table is given."""
+    lv = nf4_levels() if levels is None else levels
     c = np.asarray(codes_unpacked, dtype=np.uint8).ravel()
     blk = np.arange(c.size) // BLOCK
     out = np.empty(c.size, dtype=np.uint16)
@@ -317,7 +376,7 @@ def dequantize_codes(codes_unpacked: np.ndarray, scales: np.ndarray) -> np.ndarr
 def dequantize(q: dict, shape=None) -> np.ndarray:
     """doubleDequant of a quantized tensor -> bf16 bit patterns (flattened, or reshaped)."""
     numel = q["numel"]
-    out = dequantize_codes(unpack_nibbles(q["codes"], numel), q["scales"])
+    out = dequantize_codes(unpack_nibbles(q["codes"], numel), q["scales"], codebook_levels(q.get("codebook", "nf4")))
     return out.reshape(shape) if shape is not None else out
 
 

@@ -52,6 +52,27 @@ def test_library_codebook_matches_oracle(lib):
     assert np.array_equal(by_thr, nf4.nearest_level(x))
 
 
+@pytest.mark.parametrize("cb,name", [(0, "nf4"), (1, "fp4"), (2, "int4")])
+def test_library_codebook_tables_match_oracle(lib, cb, name):
+    """Every table the library offers equals the oracle's bit for bit, and encoding with its
+    thresholds equals the oracle's nearest level."""
+    lv = (C.c_float * 16)()
+    th = (C.c_float * 15)()
+    assert lib.qlora_codebook_table(cb, lv, th) == 0
+    lv = np.array(lv, dtype=np.float32)
+    th = np.array(th, dtype=np.float32)
+    ref = nf4.codebook_levels(name)
+    assert np.array_equal(lv.view(np.uint32), ref.view(np.uint32))
+    mids = (lv.astype(np.float64)[:-1] + lv.astype(np.float64)[1:]) / 2
+    assert np.all(th.astype(np.float64) <= mids)
+    assert np.all(np.nextafter(th, np.float32(2)).astype(np.float64) > mids)
+    rng = np.random.default_rng(cb)
+    x = np.concatenate([rng.uniform(-1, 1, 100_000).astype(np.float32), th, np.nextafter(th, np.float32(2))])
+    assert np.array_equal((x[:, None] > th[None, :]).sum(axis=1), nf4.nearest_level(x, ref))
+    assert lib.qlora_codebook_table(3, lv.ctypes.data_as(C.POINTER(C.c_float)), None) == 4
+    assert lib.qlora_codebook_table(-1, None, None) == 4
+
+
 @pytest.mark.parametrize("rows,cols,dq", [(4096, 4096, 1), (256, 256, 0), (3, 77, 1), (1, 1, 1), (22016, 8192, 1)])
 def test_sizes_match_oracle(lib, rows, cols, dq):
     out = [C.c_size_t() for _ in range(4)]
@@ -77,8 +98,8 @@ def test_workspace_queries(lib):
     assert lib.qlora_fwd_workspace(16, 4096, 4096, 300) == 0
 
 
-def _desc(rows=256, cols=256, dq=1, codes=0x10000, absmax=0x20000, c1=0x30000, mu=0x40000):
-    return _lib.qlora_nf4(rows, cols, dq, 0, codes, absmax, c1, mu)
+def _desc(rows=256, cols=256, dq=1, codes=0x10000, absmax=0x20000, c1=0x30000, mu=0x40000, cb=0):
+    return _lib.qlora_nf4(rows, cols, dq, cb, codes, absmax, c1, mu)
 
 
 def test_validation_errors_return_before_any_launch(lib):
@@ -102,6 +123,8 @@ def test_validation_errors_return_before_any_launch(lib):
     for r in (0, 4, 12, 264):
         assert fwd(ok, 16, C.byref(d), ok, ok, r, 2.0, ok, None, ws, big, None) == 4
     assert fwd(ok, 16, C.byref(_desc(dq=3)), ok, ok, 8, 2.0, ok, None, ws, big, None) == 4
+    assert fwd(ok, 16, C.byref(_desc(cb=3)), ok, ok, 8, 2.0, ok, None, ws, big, None) == 4
+    assert lib.qlora_quantize_nf4(ok, 256, 256, C.byref(_desc(cb=-1)), ws, big, None) == 4
     # alignment
     assert fwd(C.c_void_p(0x100002), 16, C.byref(d), ok, ok, 8, 2.0, ok, None, ws, big, None) == 3
     assert fwd(ok, 16, C.byref(_desc(codes=0x10008)), ok, ok, 8, 2.0, ok, None, ws, big, None) == 3

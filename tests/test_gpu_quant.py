@@ -12,19 +12,19 @@ from oracle import nf4
 pytestmark = pytest.mark.gpu
 
 
-def _gpu_quant(w_u16: np.ndarray, shape, dq: bool):
+def _gpu_quant(w_u16: np.ndarray, shape, dq: bool, codebook="nf4"):
     require_gpu()
     W = dev_bf16(w_u16.reshape(-1)).reshape(shape)
-    q = Q.qlora_quantize_nf4(W, double_quant=dq)
+    q = Q.qlora_quantize_nf4(W, double_quant=dq, codebook=Q.CODEBOOKS[codebook])
     deq = Q.qlora_dequant(q)
     torch.cuda.synchronize()
     return q, deq
 
 
-def _check(w_u16: np.ndarray, shape, dq: bool, label: str):
-    log("quantize", label, shape, "dq" if dq else "no-dq")
-    q, deq = _gpu_quant(w_u16, shape, dq)
-    ref = nf4.quantize(w_u16, double_quant=dq)
+def _check(w_u16: np.ndarray, shape, dq: bool, label: str, codebook="nf4"):
+    log("quantize", label, shape, "dq" if dq else "no-dq", codebook)
+    q, deq = _gpu_quant(w_u16, shape, dq, codebook)
+    ref = nf4.quantize(w_u16, double_quant=dq, codebook=codebook)
     codes = host(q.codes)
     bad = np.flatnonzero(codes != ref["codes"])
     assert bad.size == 0, f"{label}: {bad.size} code bytes differ, first at byte {bad[:5]}"
@@ -47,6 +47,16 @@ def _check(w_u16: np.ndarray, shape, dq: bool, label: str):
 def test_quantize_small_shapes(shape, dq):
     w = workloads.normal_bf16(7 + shape[0], shape, 0.02)
     _check(w, shape, dq, f"gauss{shape}")
+
+
+@pytest.mark.parametrize("codebook", ["fp4", "int4"])
+@pytest.mark.parametrize("shape,dq", [((256, 256), True), ((256, 256), False), ((3, 77), True),
+                                      ((4096, 4096), True)])
+def test_quantize_other_codebooks(codebook, shape, dq):
+    """FP4 and Int4 tables through the same kernels: codes, constants and dequantized
+    weights bit-exact (ragged tails hold the tables' zero code, index 8)."""
+    w = workloads.normal_bf16(11 + shape[1], shape, 0.02)
+    _check(w, shape, dq, f"{codebook}{shape}", codebook)
 
 
 def test_quantize_c1_config():
