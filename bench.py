@@ -21,6 +21,7 @@ Also reported:
                   rotating 6 weight copies (> 512 MB) per shape;
   quantize     -- quantize + double-quantize of the headline weight (timed apart):
                   bytes moved (bf16 in, codes and constants out) over time;
+  adamw        -- one AdamW step on the adapters (fp32 state), GB/s against 8 TB/s;
   formats      -- quantization error (relative MSE of the dequantized weight) of the
                   NF4, FP4 and Int4 tables on the headline weight shape;
   mlp_7b, stack_65b -- forward+backward TFLOP/s over the 7B MLP pair (M = 4096)
@@ -92,7 +93,7 @@ def parse():
     ap.add_argument("--gemv-iters", type=int, default=50)
     ap.add_argument("--no-layers", action="store_true", help="skip the 7B MLP pair and the 65B layer stack")
     ap.add_argument("--layer-steps", type=int, default=3, help="timed steps of the 7B MLP pair and the 65B stack")
-    ap.add_argument("--only", choices=["all", "headline", "gemv", "layers", "copy"], default="all",
+    ap.add_argument("--only", choices=["all", "headline", "gemv", "layers", "adamw", "copy"], default="all",
                     help="restrict the run (for profiling single kernels); 'copy' runs a plain device copy of "
                          "known size, the reference for scaling hardware byte counters")
     return ap.parse_args()
@@ -242,6 +243,9 @@ def main():
 
     if args.only in ("all", "headline"):
         result["formats"] = bench_formats(Q, workloads, torch, dev)
+
+    if args.only in ("all", "adamw"):
+        result["adamw"] = bench_adamw(Q, torch, dev)
 
     if args.only in ("all", "layers") and not args.no_layers:
         result["mlp_7b"] = bench_layers(Q, workloads, torch, dev, 3, args.layer_steps, 1)
@@ -412,6 +416,36 @@ def bench_formats(Q, workloads, torch, dev):
         del q, d
     out["order"] = " < ".join(sorted(Q.CODEBOOKS, key=lambda k: out[k]["rel_mse"]))
     torch.cuda.empty_cache()
+    return out
+
+
+def bench_adamw(Q, torch, dev, iters=10):
+    """AdamW step on the adapters: the 4096->4096 rank-64 adapter (A and B, 524,288
+    parameters) and the whole 65B stack's adapters as one buffer (80 x 7 linears at
+    rank 64: 799,539,200 parameters).  Bytes per parameter: fp32 param, grad, m, v read
+    (16) and param, m, v written (12) plus the bf16 working copy (2)."""
+    out = {"bytes_per_param": 30, "peak_GBps": PEAK_HBM_GBPS}
+    for name, n in (("adapter_4096x4096_r64", 2 * 4096 * 64), ("stack_65b_adapters", 799_539_200)):
+        g = torch.Generator(device=dev)
+        g.manual_seed(3000)
+        p = torch.randn(n, generator=g, device=dev, dtype=torch.float32).mul_(0.02)
+        grad = torch.randn(n, generator=g, device=dev, dtype=torch.float32).mul_(1e-3)
+        m = torch.zeros(n, device=dev, dtype=torch.float32)
+        v = torch.zeros(n, device=dev, dtype=torch.float32)
+        pb = torch.empty(n, device=dev, dtype=torch.bfloat16)
+        for t in range(1, 3):
+            Q.qlora_adamw_step(p, grad, m, v, t, 2e-4, weight_decay=0.01, param_bf16=pb)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for t in range(3, 3 + iters):
+            Q.qlora_adamw_step(p, grad, m, v, t, 2e-4, weight_decay=0.01, param_bf16=pb)
+        e1.record()
+        torch.cuda.synchronize()
+        us = 1e3 * e0.elapsed_time(e1) / iters
+        out[name] = {"params": n, "us_per_step": us, "GBps": 30 * n / (us * 1e-6) / 1e9}
+        del p, grad, m, v, pb
+        torch.cuda.empty_cache()
     return out
 
 

@@ -18,7 +18,7 @@ __all__ = [
     "NF4Weight", "QLoRAError", "nf4_alloc", "qlora_nf4_codebook", "qlora_codebook_table", "qlora_nf4_sizes",
     "CODEBOOK_NF4", "CODEBOOK_FP4", "CODEBOOK_INT4", "CODEBOOKS", "qlora_quantize_workspace",
     "qlora_fwd_workspace", "qlora_bwd_workspace", "qlora_quantize_nf4", "qlora_dequant", "qlora_linear_fwd",
-    "qlora_linear_bwd", "qlora_profile_enable", "qlora_profile_read", "lib",
+    "qlora_linear_bwd", "qlora_adamw_step", "qlora_profile_enable", "qlora_profile_read", "lib",
 ]
 
 
@@ -197,6 +197,23 @@ def qlora_linear_bwd(dY: torch.Tensor, X: torch.Tensor, T_saved: torch.Tensor | 
                                   float(scale), _ptr(dX if need_dX else None), _ptr(dA), _ptr(dB), _ptr(ws),
                                   0 if ws is None else ws.numel(), _stream(stream)), "qlora_linear_bwd")
     return (dX if need_dX else None), dA, dB
+
+
+def qlora_adamw_step(param: torch.Tensor, grad: torch.Tensor, m: torch.Tensor, v: torch.Tensor, step: int,
+                     lr: float, beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8,
+                     weight_decay: float = 0.0, param_bf16: torch.Tensor | None = None, stream=None):
+    """One AdamW step in place on fp32 `param`, `m`, `v` (same number of elements as the
+    fp32 `grad`); writes bf16(param) into `param_bf16` when given."""
+    n = param.numel()
+    for t, name in ((param, "param"), (grad, "grad"), (m, "m"), (v, "v")):
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != n:
+            raise QLoRAError(f"{name} must be a contiguous float32 tensor of {n} elements")
+    if param_bf16 is not None and (param_bf16.dtype != torch.bfloat16 or param_bf16.numel() != n
+                                   or not param_bf16.is_contiguous()):
+        raise QLoRAError("param_bf16 must be a contiguous bf16 tensor of the same size")
+    _check(lib().qlora_adamw_step(_ptr(param), _ptr(param_bf16), _ptr(grad), _ptr(m), _ptr(v), n, int(step),
+                                  float(lr), float(beta1), float(beta2), float(eps), float(weight_decay),
+                                  _stream(stream)), "qlora_adamw_step")
 
 
 def qlora_profile_enable(enable: bool = True):

@@ -436,4 +436,18 @@ int32_t qlora_profile_read(qlora_kernel_time* outp, int32_t max_entries, int32_t
   return n;
 }
 
+qlora_status qlora_adamw_step(float* param, uint16_t* param_bf16, const float* grad, float* m, float* v, int64_t n,
+                              int64_t step, float lr, float beta1, float beta2, float eps, float weight_decay,
+                              hipStream_t stream) {
+  if (n < 0 || step < 1) return QLORA_ERR_SHAPE;
+  if (!(beta1 >= 0.0f && beta1 < 1.0f && beta2 >= 0.0f && beta2 < 1.0f && eps > 0.0f)) return QLORA_ERR_UNSUPPORTED;
+  if (n == 0) return QLORA_OK;
+  if (!param || !grad || !m || !v) return QLORA_ERR_NULL;
+  if (!aligned16(param) || !aligned16(grad) || !aligned16(m) || !aligned16(v) ||
+      (param_bf16 && (reinterpret_cast<uintptr_t>(param_bf16) & 7u)))
+    return QLORA_ERR_ALIGN;
+  QL_HIP(launch_adamw(param, param_bf16, grad, m, v, n, step, lr, beta1, beta2, eps, weight_decay, stream));
+  return QLORA_OK;
+}
+
 }  // extern "C"

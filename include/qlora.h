@@ -169,6 +169,23 @@ qlora_status qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, const uint1
                               const qlora_nf4* w, const uint16_t* A, const uint16_t* B, int32_t r, float scale,
                               uint16_t* dX, float* dA, float* dB, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* One AdamW step on n adapter parameters ("Paged optimizers": only the adapters carry
+ * gradients and optimizer state, kept in fp32).  With t = step (>= 1), in fp32 with each
+ * product and sum rounded separately, the bias corrections formed on the host in float64:
+ *   p <- p * (1 - lr wd)
+ *   m <- beta1 m + (1 - beta1) g
+ *   v <- beta2 v + (1 - beta2) g^2
+ *   p <- p - (lr / (1 - beta1^t)) m / (sqrt(v) / sqrt(1 - beta2^t) + eps)
+ * param, m, v are updated in place; if param_bf16 is not NULL, bf16_RNE(p) is written there
+ * (the working copy qlora_linear_fwd/bwd read as A or B).  grad is dA or dB from
+ * qlora_linear_bwd.  The state may live in any memory the GPU can address (device memory,
+ * or host memory the caller has made device-accessible to page the state out).
+ * Requires: n >= 0 (0 is a no-op); step >= 1; 0 <= beta1, beta2 < 1; eps > 0; param, grad,
+ * m, v non-NULL and 16-byte aligned, param_bf16 8-byte aligned; no overlap.             */
+qlora_status qlora_adamw_step(float* param, uint16_t* param_bf16, const float* grad, float* m, float* v, int64_t n,
+                              int64_t step, float lr, float beta1, float beta2, float eps, float weight_decay,
+                              hipStream_t stream);
+
 /* Optional per-kernel timing, for benchmarking.  While enabled, every kernel
  * launch of this library is bracketed by HIP events on its stream.
  * qlora_profile_read synchronizes those events and returns, per kernel name,

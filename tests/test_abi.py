@@ -149,6 +149,19 @@ def test_validation_errors_return_before_any_launch(lib):
     assert lib.qlora_dequant(None, ok, None) == 1
 
 
+def test_adamw_validation(lib):
+    ok = C.c_void_p(0x100000)
+    f = lib.qlora_adamw_step
+    assert f(None, None, None, None, None, 0, 1, 1e-3, 0.9, 0.999, 1e-8, 0.0, None) == 0   # n = 0: no-op
+    assert f(ok, None, ok, ok, ok, -1, 1, 1e-3, 0.9, 0.999, 1e-8, 0.0, None) == 2
+    assert f(ok, None, ok, ok, ok, 8, 0, 1e-3, 0.9, 0.999, 1e-8, 0.0, None) == 2
+    assert f(ok, None, ok, ok, ok, 8, 1, 1e-3, 1.0, 0.999, 1e-8, 0.0, None) == 4
+    assert f(ok, None, ok, ok, ok, 8, 1, 1e-3, 0.9, 0.999, 0.0, 0.0, None) == 4
+    assert f(ok, None, None, ok, ok, 8, 1, 1e-3, 0.9, 0.999, 1e-8, 0.0, None) == 1
+    assert f(C.c_void_p(0x100004), None, ok, ok, ok, 8, 1, 1e-3, 0.9, 0.999, 1e-8, 0.0, None) == 3
+    assert f(ok, C.c_void_p(0x100002), ok, ok, ok, 8, 1, 1e-3, 0.9, 0.999, 1e-8, 0.0, None) == 3
+
+
 def test_status_strings(lib):
     for s in range(7):
         assert lib.qlora_status_str(s)
