@@ -22,6 +22,8 @@ Also reported:
   quantize     -- quantize + double-quantize of the headline weight (timed apart):
                   bytes moved (bf16 in, codes and constants out) over time;
   adamw        -- one AdamW step on the adapters (fp32 state), GB/s against 8 TB/s;
+  merge        -- adapter merge + requantize on the headline layer: times, and the
+                  output error the requantization leaves;
   formats      -- quantization error (relative MSE of the dequantized weight) of the
                   NF4, FP4 and Int4 tables on the headline weight shape;
   mlp_7b, stack_65b -- forward+backward TFLOP/s over the 7B MLP pair (M = 4096)
@@ -243,6 +245,7 @@ def main():
 
     if args.only in ("all", "headline"):
         result["formats"] = bench_formats(Q, workloads, torch, dev)
+        result["merge"] = bench_merge(Q, workloads, torch, dev)
 
     if args.only in ("all", "adamw"):
         result["adamw"] = bench_adamw(Q, torch, dev)
@@ -415,6 +418,48 @@ def bench_formats(Q, workloads, torch, dev):
         out[name] = {"rel_mse": ((d - w) ** 2).mean().item() / den}
         del q, d
     out["order"] = " < ".join(sorted(Q.CODEBOOKS, key=lambda k: out[k]["rel_mse"]))
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_merge(Q, workloads, torch, dev, iters=10):
+    """Adapter merge + requantize on the headline layer (4096x4096, r = 64, s = 0.25):
+    time of qlora_merge_adapter and of requantizing its bf16 output, and the error the
+    requantization leaves in the layer's output on 2048 tokens:
+    |X deq(requant(W'))^T - Y| / |Y| with Y the unmerged layer (base + adapter), beside the
+    size of the adapter's own contribution |Y - X deq(W)^T| / |Y|."""
+    M, din, dout, r, s = 2048, 4096, 4096, 64, 0.25
+    W = workloads.device_normal_bf16(2600, (dout, din), 0.02)
+    A = workloads.device_normal_bf16(2601, (din, r), 0.02)
+    B = workloads.device_normal_bf16(2602, (r, dout), 0.02)
+    X = workloads.device_normal_bf16(2603, (M, din), 1.0)
+    w = Q.qlora_quantize_nf4(W, True)
+    Wm = torch.empty((dout, din), dtype=torch.bfloat16, device=dev)
+    wm = Q.nf4_alloc(dout, din, True, dev)
+    ws = torch.empty(Q.qlora_quantize_workspace(dout, din), dtype=torch.uint8, device=dev)
+    for _ in range(2):
+        Q.qlora_merge_adapter(w, A, B, s, out=Wm)
+        Q.qlora_quantize_nf4(Wm, True, out=wm, workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    e0.record()
+    for _ in range(iters):
+        Q.qlora_merge_adapter(w, A, B, s, out=Wm)
+    e1.record()
+    for _ in range(iters):
+        Q.qlora_quantize_nf4(Wm, True, out=wm, workspace=ws)
+    e2.record()
+    torch.cuda.synchronize()
+    Y, _ = Q.qlora_linear_fwd(X, w, A, B, s, save_T=False)
+    Z = torch.zeros_like(B)
+    Ym, _ = Q.qlora_linear_fwd(X, wm, A, Z, s, save_T=False)
+    Yb, _ = Q.qlora_linear_fwd(X, w, A, Z, s, save_T=False)
+    y, ym, yb = Y.float(), Ym.float(), Yb.float()
+    ny = torch.linalg.vector_norm(y).item()
+    out = {"merge_us": 1e3 * e0.elapsed_time(e1) / iters, "requantize_us": 1e3 * e1.elapsed_time(e2) / iters,
+           "output_rel_err_merged_requantized": torch.linalg.vector_norm(ym - y).item() / ny,
+           "output_rel_size_of_adapter_term": torch.linalg.vector_norm(y - yb).item() / ny}
+    del W, A, B, X, w, Wm, wm, ws, Y, Ym, Yb, Z
     torch.cuda.empty_cache()
     return out
 

@@ -18,7 +18,7 @@ __all__ = [
     "NF4Weight", "QLoRAError", "nf4_alloc", "qlora_nf4_codebook", "qlora_codebook_table", "qlora_nf4_sizes",
     "CODEBOOK_NF4", "CODEBOOK_FP4", "CODEBOOK_INT4", "CODEBOOKS", "qlora_quantize_workspace",
     "qlora_fwd_workspace", "qlora_bwd_workspace", "qlora_quantize_nf4", "qlora_dequant", "qlora_linear_fwd",
-    "qlora_linear_bwd", "qlora_adamw_step", "qlora_profile_enable", "qlora_profile_read", "lib",
+    "qlora_linear_bwd", "qlora_merge_adapter", "qlora_adamw_step", "qlora_profile_enable", "qlora_profile_read", "lib",
 ]
 
 
@@ -197,6 +197,18 @@ def qlora_linear_bwd(dY: torch.Tensor, X: torch.Tensor, T_saved: torch.Tensor | 
                                   float(scale), _ptr(dX if need_dX else None), _ptr(dA), _ptr(dB), _ptr(ws),
                                   0 if ws is None else ws.numel(), _stream(stream)), "qlora_linear_bwd")
     return (dX if need_dX else None), dA, dB
+
+
+def qlora_merge_adapter(w: NF4Weight, A: torch.Tensor, B: torch.Tensor, scale: float,
+                        out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """bf16 [rows][cols] weight deq(W) + scale (A B)^T (requantize it with qlora_quantize_nf4)."""
+    _bf16(A, "A"); _bf16(B, "B")
+    if out is None:
+        out = torch.empty((w.rows, w.cols), dtype=torch.bfloat16, device=A.device)
+    d = w.desc()
+    _check(lib().qlora_merge_adapter(C.byref(d), _ptr(A), _ptr(B), A.shape[1], float(scale), _ptr(out),
+                                     _stream(stream)), "qlora_merge_adapter")
+    return out
 
 
 def qlora_adamw_step(param: torch.Tensor, grad: torch.Tensor, m: torch.Tensor, v: torch.Tensor, step: int,

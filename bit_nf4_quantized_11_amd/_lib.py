@@ -41,6 +41,8 @@ SIGNATURES = {
     "qlora_version": (C.c_char_p, []),
     "qlora_nf4_codebook": (C.c_int, [C.POINTER(C.c_float), C.POINTER(C.c_float)]),
     "qlora_codebook_table": (C.c_int, [C.c_int32, C.POINTER(C.c_float), C.POINTER(C.c_float)]),
+    "qlora_merge_adapter": (C.c_int, [C.POINTER(qlora_nf4), C.c_void_p, C.c_void_p, C.c_int32, C.c_float, C.c_void_p,
+                                      C.c_void_p]),
     "qlora_adamw_step": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64, C.c_int64,
                                    C.c_float, C.c_float, C.c_float, C.c_float, C.c_float, C.c_void_p]),
     "qlora_nf4_sizes": (C.c_int, [C.c_int64, C.c_int64, C.c_int32, C.POINTER(C.c_size_t), C.POINTER(C.c_size_t),

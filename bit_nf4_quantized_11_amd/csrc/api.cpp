@@ -436,6 +436,16 @@ int32_t qlora_profile_read(qlora_kernel_time* outp, int32_t max_entries, int32_t
   return n;
 }
 
+qlora_status qlora_merge_adapter(const qlora_nf4* w, const uint16_t* A, const uint16_t* B, int32_t r, float scale,
+                                 uint16_t* W_out, hipStream_t stream) {
+  const qlora_status st = check_linear(0, w, r);
+  if (st != QLORA_OK) return st;
+  if (!A || !B || !W_out) return QLORA_ERR_NULL;
+  if (!aligned16(A) || !aligned16(B) || !aligned16(W_out)) return QLORA_ERR_ALIGN;
+  QL_HIP(launch_merge_adapter(view_of(w), w->rows, w->cols, A, B, r, scale, W_out, stream));
+  return QLORA_OK;
+}
+
 qlora_status qlora_adamw_step(float* param, uint16_t* param_bf16, const float* grad, float* m, float* v, int64_t n,
                               int64_t step, float lr, float beta1, float beta2, float eps, float weight_decay,
                               hipStream_t stream) {

@@ -107,6 +107,10 @@ hipError_t launch_dx_gemm(const uint16_t* dY, int64_t M, int64_t K, int64_t N, c
                           const uint16_t* Gs, int64_t rp, const uint16_t* A, int64_t r, uint16_t* dX,
                           hipStream_t s);
 
+// ---- adapter merge (merge.hip): out [N][K] = bf16(deq(W) + scale (A B)^T), K % 64 == 0 -------
+hipError_t launch_merge_adapter(const NF4View& w, int64_t N, int64_t K, const uint16_t* A, const uint16_t* B, int64_t r,
+                                float scale, uint16_t* out, hipStream_t s);
+
 // ---- AdamW step on adapter parameters (adamw.hip) ------------------------------------------
 hipError_t launch_adamw(float* param, uint16_t* param_bf16, const float* grad, float* m, float* v, int64_t n,
                         int64_t step, float lr, float beta1, float beta2, float eps, float weight_decay,

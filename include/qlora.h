@@ -169,6 +169,18 @@ qlora_status qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, const uint1
                               const qlora_nf4* w, const uint16_t* A, const uint16_t* B, int32_t r, float scale,
                               uint16_t* dX, float* dA, float* dB, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Merge the adapter into the base weight ("QLoRA: quantising the part you are not
+ * training", section "What it costs": merging into the quantised base means
+ * requantising): W_out [out][in] bf16 with
+ *   W_out[n][k] = bf16_RNE( fl32( deq(W)[n][k] + fl32(scale * d) ) ),
+ *   d = fp32 fused multiply-add chain over j = 0..r-1 of A[k][j] * B[j][n],
+ * deq(W) the bf16 dequantized weight of the qlora_nf4 comment.  Quantize W_out again
+ * with qlora_quantize_nf4 to get a merged 4-bit weight.  Same shape and alignment
+ * rules as qlora_linear_fwd (in % 64 == 0, out % 8 == 0, r % 8 == 0, 8 <= r <= 256,
+ * 16-byte aligned pointers).                                                        */
+qlora_status qlora_merge_adapter(const qlora_nf4* w, const uint16_t* A, const uint16_t* B, int32_t r, float scale,
+                                 uint16_t* W_out, hipStream_t stream);
+
 /* One AdamW step on n adapter parameters ("Paged optimizers": only the adapters carry
  * gradients and optimizer state, kept in fp32).  With t = step (>= 1), in fp32 with each
  * product and sum rounded separately, the bias corrections formed on the host in float64:

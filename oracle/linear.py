@@ -74,3 +74,10 @@ def flops_fwd(M, d_in, d_out, r) -> int:
 def flops_fwd_bwd(M, d_in, d_out, r) -> int:
     """fwd (2 M in out + 2 M r (in+out)) + bwd without dW (2 M in out + 4 M r (in+out))."""
     return 4 * M * d_in * d_out + 6 * M * r * (d_in + d_out)
+
+
+def merge_adapter(Wq, A, B, s: float):
+    """The merged weight deq(W) + s (A B)^T [out][in] in float64 with no rounding
+    ("QLoRA: quantising the part you are not training", section "What it costs": merging
+    the adapter into the base).  Wq is the bf16 dequantized weight [out][in]."""
+    return _f64(Wq) + s * (_f64(A) @ _f64(B)).T

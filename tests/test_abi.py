@@ -149,6 +149,18 @@ def test_validation_errors_return_before_any_launch(lib):
     assert lib.qlora_dequant(None, ok, None) == 1
 
 
+def test_merge_validation(lib):
+    ok = C.c_void_p(0x100000)
+    d = _desc()
+    f = lib.qlora_merge_adapter
+    assert f(C.byref(d), None, ok, 8, 0.25, ok, None) == 1
+    assert f(C.byref(d), ok, ok, 8, 0.25, None, None) == 1
+    assert f(None, ok, ok, 8, 0.25, ok, None) == 1
+    assert f(C.byref(_desc(cols=100)), ok, ok, 8, 0.25, ok, None) == 2
+    assert f(C.byref(d), ok, ok, 12, 0.25, ok, None) == 4
+    assert f(C.byref(d), ok, C.c_void_p(0x100008), 8, 0.25, ok, None) == 3
+
+
 def test_adamw_validation(lib):
     ok = C.c_void_p(0x100000)
     f = lib.qlora_adamw_step

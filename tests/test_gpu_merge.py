@@ -1,0 +1,48 @@
+"""GPU parity of the adapter merge W' = bf16(deq(W) + s (A B)^T) against the float64
+oracle: every element within one bf16 step of the exact merged value plus the fp32
+roundings of the rank-r term and of the sum (the kernel accumulates in fp32 and rounds
+twice), nearly all equal to its correctly rounded value; and the merged weight requantizes bit-exactly like the oracle's quantizer."""
+import numpy as np
+import pytest
+import torch
+
+import bit_nf4_quantized_11_amd as Q
+import workloads
+from helpers import dev_bf16, host, host_u16, log, require_gpu
+from oracle import linear, nf4
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf16_ulp(x):
+    e = np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -126)))
+    return 2.0 ** (e - 7)
+
+
+@pytest.mark.parametrize("M,din,dout,r,dq,cb", [(4, 320, 264, 8, True, "nf4"), (4, 256, 128, 72, False, "nf4"),
+                                                (4, 512, 256, 256, True, "fp4"), (4, 4096, 4096, 64, True, "nf4")])
+def test_merge_matches_oracle(M, din, dout, r, dq, cb):
+    require_gpu()
+    inp = workloads.custom_linear(M, din, dout, r, seed=din + dout + r)
+    log("merge", din, dout, r, dq, cb)
+    w = Q.qlora_quantize_nf4(dev_bf16(inp.W), double_quant=dq, codebook=Q.CODEBOOKS[cb])
+    s = 0.25
+    Wm = Q.qlora_merge_adapter(w, dev_bf16(inp.A), dev_bf16(inp.B), s)
+    torch.cuda.synchronize()
+    got = host_u16(Wm)
+    Wd = nf4.dequantize(nf4.quantize(inp.W, double_quant=dq, codebook=cb), (dout, din))
+    exact = linear.merge_adapter(Wd, inp.A, inp.B, s)
+    g = nf4.bf16_to_f32(got).astype(np.float64)
+    # one bf16 step of the result, plus the fp32 roundings of the adapter term and of the sum,
+    # which dominate where deq(W) and the adapter term cancel
+    mag = np.abs(nf4.bf16_to_f32(Wd).astype(np.float64)) + s * (np.abs(nf4.bf16_to_f32(inp.A).astype(np.float64))
+                                                                @ np.abs(nf4.bf16_to_f32(inp.B).astype(np.float64))).T
+    bound = _bf16_ulp(exact) + (r + 2) * 2.0 ** -24 * mag
+    assert np.all(np.abs(g - exact) <= bound), "merged weight off by more than a bf16 step and fp32 roundings"
+    rne = nf4.f32_to_bf16(exact.astype(np.float32))
+    assert np.mean(got == rne) > 0.999
+    # requantize the merged weight: bit-exact with the oracle's quantizer on the same bf16 input
+    q2 = Q.qlora_quantize_nf4(Wm, double_quant=dq, codebook=Q.CODEBOOKS[cb])
+    torch.cuda.synchronize()
+    ref = nf4.quantize(got, double_quant=dq, codebook=cb)
+    assert np.array_equal(host(q2.codes), ref["codes"])

@@ -124,3 +124,16 @@ def test_review_page_gradients_with_unit_scale():
 def test_flop_counts():
     assert linear.flops_fwd_bwd(2048, 4096, 4096, 64) == 143_881_404_416
     assert linear.flops_fwd(1, 8192, 22016, 64) == 2 * 8192 * 22016 + 2 * 64 * (8192 + 22016)
+
+
+def test_merged_weight_reproduces_the_layer():
+    """X merged^T equals the layer's forward in exact arithmetic (the adapter term folds
+    into the weight by distributivity); B = 0 leaves the dequantized weight unchanged."""
+    inp, Wd = _case(M=12, d_in=128, d_out=64, r=8, seed=9)
+    s = 2.0
+    Wm = linear.merge_adapter(Wd, inp.A, inp.B, s)
+    y, _ = linear.forward(inp.X, Wd, inp.A, inp.B, s)
+    x = nf4.bf16_to_f32(inp.X).astype(np.float64)
+    np.testing.assert_allclose(x @ Wm.T, y, rtol=1e-12, atol=1e-12)
+    W0 = linear.merge_adapter(Wd, inp.A, np.zeros_like(inp.B), s)
+    np.testing.assert_array_equal(W0, nf4.bf16_to_f32(Wd).astype(np.float64).reshape(64, 128))
