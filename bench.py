@@ -22,6 +22,8 @@ Also reported:
   quantize     -- quantize + double-quantize of the headline weight (timed apart):
                   bytes moved (bf16 in, codes and constants out) over time;
   adamw        -- one AdamW step on the adapters (fp32 state), GB/s against 8 TB/s;
+  comparators  -- the headline step on the unquantized bf16 weight and with the weight
+                  dequantized into a buffer first (torch / hipBLASLt products), as context;
   merge        -- adapter merge + requantize on the headline layer: times, and the
                   output error the requantization leaves;
   formats      -- quantization error (relative MSE of the dequantized weight) of the
@@ -246,6 +248,7 @@ def main():
     if args.only in ("all", "headline"):
         result["formats"] = bench_formats(Q, workloads, torch, dev)
         result["merge"] = bench_merge(Q, workloads, torch, dev)
+        result["comparators"] = bench_comparators(Q, workloads, torch, dev, result["ms_per_step"])
 
     if args.only in ("all", "adamw"):
         result["adamw"] = bench_adamw(Q, torch, dev)
@@ -418,6 +421,54 @@ def bench_formats(Q, workloads, torch, dev):
         out[name] = {"rel_mse": ((d - w) ** 2).mean().item() / den}
         del q, d
     out["order"] = " < ".join(sorted(Q.CODEBOOKS, key=lambda k: out[k]["rel_mse"]))
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_comparators(Q, workloads, torch, dev, ms_qlora, iters=20):
+    """Context for the headline step (never part of the library): the same forward and
+    backward with (i) the unquantized bf16 weight ("LoRA without quantization") and (ii) the
+    weight dequantized into a bf16 buffer first ("materialize then GEMM"), the products done
+    by torch's bf16 matmul (hipBLASLt) with fp32 accumulation.  The pages put QLoRA's step at
+    25-40% slower than LoRA on unquantized weights ("QLoRA: quantising the part you are not
+    training", section "What it costs")."""
+    M, din, dout, r, s = 2048, 4096, 4096, 64, 0.25
+    W = workloads.device_normal_bf16(2700, (dout, din), 0.02)
+    A = workloads.device_normal_bf16(2701, (din, r), 0.02)
+    B = workloads.device_normal_bf16(2702, (r, dout), 0.02)
+    X = workloads.device_normal_bf16(2703, (M, din), 1.0)
+    dY = workloads.device_normal_bf16(2704, (M, dout), 1.0)
+    w = Q.qlora_quantize_nf4(W, True)
+    Wt, At, Bt, Xt = W.t().contiguous(), A.t().contiguous(), B.t().contiguous(), X.t().contiguous()
+    Wd = torch.empty_like(W)
+
+    def lora_step(Wb, Wbt):
+        T = X @ A                                   # forward
+        Y = X @ Wbt + (T * s) @ B
+        G = dY @ Bt                                 # backward
+        dX = dY @ Wb + (G * s) @ At
+        dA = (Xt @ G) * s
+        dB = (T.t().contiguous() @ dY) * s
+        return Y, dX, dA, dB
+
+    def materialize_step():
+        Q.qlora_dequant(w, out=Wd)
+        return lora_step(Wd, Wd.t().contiguous())
+
+    out = {}
+    for name, fn in (("lora_unquantized_bf16", lambda: lora_step(W, Wt)), ("materialize_then_gemm", materialize_step)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / iters
+        out[name] = {"ms_per_step": ms, "qlora_step_over_this": ms_qlora / ms}
+    del W, A, B, X, dY, w, Wt, At, Bt, Xt, Wd
     torch.cuda.empty_cache()
     return out
 
