@@ -62,7 +62,8 @@ __global__ __launch_bounds__(NT) void k_bwd_dx_nf4_gemm(DxParams p) {
   // read as zero codes and scale mu; the token operand is zero there.  Columns past K
   // belong to outputs that are not stored.
   const int wrow = t >> 3, wb = (t >> 2) & 1, wq = t & 3;
-  const uint32_t wkb = k0 / 64 + wb;
+  const uint32_t wblk0 = (uint32_t)wrow * nkb + k0 / 64 + wb;   // block of this thread in stage 0
+  const uint32_t stage_blks = 64 * nkb;                          // blocks per 64-row stage
 
   const TokenSrc ds = token_src(p.dY, (uint64_t)p.M * p.N * 2, N, m0);
   const rsrc_t rC = make_rsrc(p.w.codes, p.codes_bytes);
@@ -77,7 +78,7 @@ __global__ __launch_bounds__(NT) void k_bwd_dx_nf4_gemm(DxParams p) {
       load_tokens_edge(S.T, ds, it * 64, N);
     else
       load_tokens(S.T, ds, it * 64);
-    const uint32_t blk = (it * 64 + wrow) * nkb + wkb;
+    const uint32_t blk = wblk0 + it * stage_blks;
     S.W.code = ld8(rC, blk * kBlockBytes + wq * 8);
     if constexpr (dq) {
       S.W.c2 = __builtin_amdgcn_raw_buffer_load_b8(rA, blk, 0, 0);

@@ -126,7 +126,7 @@ struct TokenRegs {
 // columns c0.. of a matrix whose every row has at least c0 + 64 columns
 __device__ __forceinline__ void load_tokens(TokenRegs& R, const TokenSrc& s, uint32_t c0) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) R.v[i] = ld16(s.r, s.row_off[i & 1] + c0 * 2 + (uint32_t)(i >> 1) * 64);
+  for (int i = 0; i < 4; ++i) R.v[i] = ld16(s.r, s.row_off[i & 1], c0 * 2 + (uint32_t)(i >> 1) * 64);
 }
 
 // columns c0..c0+63 where the rows end at ncols (a multiple of 8): chunks past the end read zero

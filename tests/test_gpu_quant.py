@@ -124,3 +124,67 @@ def test_quantize_is_deterministic():
     q2, _ = _gpu_quant(w, (2048, 2048), True)
     for a, b in [(q1.codes, q2.codes), (q1.absmax, q2.absmax), (q1.c1, q2.c1), (q1.mu, q2.mu)]:
         assert torch.equal(a, b)
+
+
+def _all_code_weight(seed: int, nan_codes: bool):
+    """A 256 x 64 weight, one block per row, whose 8-bit block constant is the row index:
+    every E4M3 code once (0x7F and 0xFF, the NaN codes, replaced by 0x7E / 0xFE unless
+    `nan_codes`), one group scale and the mean chosen by hand, random 4-bit codes."""
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 16, size=256 * 64).astype(np.uint8)
+    c2 = np.arange(256, dtype=np.uint8)
+    if not nan_codes:
+        c2[0x7F], c2[0xFF] = 0x7E, 0xFE
+    c1 = np.array([1.3125], np.float32)
+    mu = np.float32(0.0078125)
+    dev = torch.device("cuda", 0)
+    w = Q.NF4Weight(256, 64, True, torch.from_numpy(nf4.pack_nibbles(codes, codes.size)).to(dev),
+                    torch.from_numpy(c2).to(dev), torch.from_numpy(c1).to(dev),
+                    torch.from_numpy(np.array([mu], np.float32)).to(dev))
+    return w, codes, c2, c1, mu
+
+
+def test_dequant_every_fp8_block_code():
+    """The block-scale decode over all 256 E4M3 codes: s' = fl32(fl32(dec(c2) c1) + mu) and
+    the bf16 weights equal the oracle bit for bit; the two NaN codes give NaN weights."""
+    require_gpu()
+    w, codes, c2, c1, mu = _all_code_weight(17, nan_codes=True)
+    got = host_u16(Q.qlora_dequant(w)).reshape(256, 64)
+    torch.cuda.synchronize()
+    nan_rows = np.array([0x7F, 0xFF])
+    ok = np.setdiff1d(np.arange(256), nan_rows)
+    scales = nf4.block_scales_dq(c2[ok], np.repeat(c1, 1), mu)
+    want = nf4.dequantize_codes(codes.reshape(256, 64)[ok].reshape(-1), scales).reshape(-1, 64)
+    bad = np.flatnonzero(np.any(got[ok] != want, axis=1))
+    assert bad.size == 0, f"codes {ok[bad][:8]} decode differently"
+    assert np.all((got[nan_rows] & 0x7FFF) > 0x7F80), "NaN codes must dequantize to NaN"
+
+
+def test_linear_every_fp8_block_code():
+    """The same decode inside the linear kernels, exactly: with one-hot token rows and
+    B = 0 every output is a single dequantized weight times one, so the large-M forward
+    (Y = deq(W)^T), the skinny forward (16 columns of each row) and dX (= deq(W)) must
+    reproduce the oracle's bf16 weights for every non-NaN code."""
+    require_gpu()
+    dev = torch.device("cuda", 0)
+    w, codes, c2, c1, mu = _all_code_weight(19, nan_codes=False)
+    want = nf4.bf16_to_f32(nf4.dequantize_codes(codes, nf4.block_scales_dq(c2, c1, mu))).reshape(256, 64)
+    rng = np.random.default_rng(23)
+    A = dev_bf16(nf4.f32_to_bf16((rng.standard_normal(64 * 64) * 0.1).astype(np.float32))).reshape(64, 64)
+    B = torch.zeros((64, 256), dtype=torch.bfloat16, device=dev)
+    # large-M forward: X = I (64 tokens), Y[m][n] = W[n][m]
+    X = torch.eye(64, dtype=torch.bfloat16, device=dev)
+    Y, T = Q.qlora_linear_fwd(X, w, A, B, 0.5)
+    assert np.array_equal(host(Y.float()), want.T), "large-M forward differs from deq(W)^T"
+    # skinny forward: token m picks reduction index 4m
+    Xs = torch.zeros((16, 64), dtype=torch.bfloat16, device=dev)
+    Xs[torch.arange(16), 4 * torch.arange(16)] = 1
+    Ys, _ = Q.qlora_linear_fwd(Xs, w, A, B, 0.5)
+    assert np.array_equal(host(Ys.float()), want[:, 4 * np.arange(16)].T), "skinny forward differs"
+    # dX: dY = I (256 tokens), dX[m][k] = W[m][k]
+    dY = torch.eye(256, dtype=torch.bfloat16, device=dev)
+    Xb = torch.zeros((256, 64), dtype=torch.bfloat16, device=dev)
+    Tb = torch.zeros((256, 64), dtype=torch.bfloat16, device=dev)
+    dX, dA, dB = Q.qlora_linear_bwd(dY, Xb, Tb, w, A, B, 0.5)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(dX.float()), want), "dX differs from deq(W)"
