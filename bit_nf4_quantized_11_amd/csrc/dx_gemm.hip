@@ -113,6 +113,7 @@ __global__ __launch_bounds__(NT) void k_bwd_dx_nf4_gemm(DxParams p) {
     put(pl, S.W.code.x, 0, sb);
     mma_group(acc, Fb, 1);
     put(pl, S.W.code.y, 1, sb);
+    interleave_mfma_valu();
   };
 
   auto store_all = [&](const Stage& S, int sb) {

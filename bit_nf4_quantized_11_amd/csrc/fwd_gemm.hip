@@ -107,6 +107,7 @@ __global__ __launch_bounds__(NT) void k_fwd_nf4_gemm(FwdParams p) {
     put(pl, S.W.code.x, 0, sb);
     mma_group(acc, Fb, 1);
     put(pl, S.W.code.y, 1, sb);
+    interleave_mfma_valu();
   };
 
   auto store_all = [&](const Stage& S, int sb) {

@@ -214,6 +214,19 @@ __device__ __forceinline__ void mma_group(Acc& a, const Frags& F, int f) {
   for (int m = 0; m < 4; ++m) a.c[f][m] = mfma32(F.fa[f], F.tb[m], a.c[f][m]);
 }
 
+// Scheduling hint for one main-loop stage of a wave (16 MFMAs next to about 70 VALU
+// instructions of dequantization): MFMAs in pairs, each pair followed by up to eight VALU
+// instructions.  Left to itself the scheduler clusters the MFMAs of one of the two stages
+// of a loop trip ahead of all of that stage's dequantization, which leaves the matrix core
+// idle while the wave works through it; measured, the pairing is 5-7 % faster.
+__device__ __forceinline__ void interleave_mfma_valu() {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // VALU
+  }
+}
+
 // This wave's half of one 64-deep stage, without interleaved work (tail and adapter stages).
 template <bool NATURAL>
 __device__ __forceinline__ void mma_stage(Acc& a, const uint16_t* __restrict__ sT, const uint16_t* __restrict__ sF) {
