@@ -85,6 +85,22 @@ def test_options_no_double_quant_recompute_T_skip_dX():
     _check_full(inp, need_dX=False, label="no-dX")
 
 
+RANK_R = [
+    # (M, in, out, r): thousands of token rows for the rank-r products T = X A, G = dY B^T
+    # and the adapter gradients, with ragged tails
+    (2049, 1024, 1032, 24),    # ragged token tile, reduction of G not a multiple of 64, rank padded
+    (1024, 1024, 1024, 256),   # largest rank
+    (2048, 2048, 1088, 8),     # smallest rank
+]
+
+
+@pytest.mark.parametrize("M,din,dout,r", RANK_R)
+def test_many_token_rank_products(M, din, dout, r):
+    inp = workloads.custom_linear(M, din, dout, r, seed=M + din + dout + r)
+    _check_full(inp, label=f"rank-r{(M, din, dout, r)}")
+    _check_full(inp, save_T=False, label=f"rank-r{(M, din, dout, r)} recompute-T")
+
+
 @pytest.mark.parametrize("dq", [True, False])
 def test_skinny_ragged_reduction_and_rows(dq):
     """Skinny path with a reduction of 5 blocks (one weight slice, most of its waves past
