@@ -44,6 +44,12 @@ Readings where the pages leave a step open (each is listed in the design notes):
   R10 s' = fl32(fl32(dec(c2) * c1) + mu), two roundings, no fused multiply-add;
   R11 the codes use the true absmax; dequant uses s';
   R12 dequantized weight = bf16_RNE(fl32(level[code] * s')).
+  R20 other block sizes (32, 128, 256; [Explainer] "Double quantization": smaller blocks
+      are more precise and cost more constants, larger blocks the reverse): one constant
+      per `block` contiguous weights, double quantization still in groups of 256
+      constants; the code layout of R6 is unchanged (it is defined per 8-element group)
+      and the code buffer is padded with the zero code to whole blocks and to a whole
+      number of 64-element chunks.
 """
 from __future__ import annotations
 
@@ -53,6 +59,7 @@ import numpy as np
 
 OFFSET = 0.9677083      # [Explainer] "NormalFloat", code-point listing
 BLOCK = 64              # [Explainer] "Quantize in blocks"; [Addaly] "NF4, and why not plain int4"
+BLOCKS = (32, 64, 128, 256)   # block sizes of the format variants (reading R20)
 SUPER = 256             # [Explainer] "Double quantization"; [Addaly] same section
 FP8_MAX = 448.0         # largest finite OCP E4M3 value (reading R7)
 FP32_MIN_NORMAL = 2.0 ** -126
@@ -161,26 +168,33 @@ def zero_code(levels: np.ndarray) -> int:
     return int(idx[0])
 
 
-def num_blocks(numel: int) -> int:
-    return -(-numel // BLOCK)
+def num_blocks(numel: int, block: int = BLOCK) -> int:
+    return -(-numel // block)
+
+
+def code_elems(numel: int, block: int = BLOCK) -> int:
+    """Elements the code buffer holds: whole blocks, and a whole number of 64-element
+    chunks of 32 bytes (reading R20)."""
+    unit = max(block, 64)
+    return -(-numel // unit) * unit
 
 
 def num_super(nblk: int) -> int:
     return -(-nblk // SUPER)
 
 
-def _blocks_f32(w_bits: np.ndarray) -> np.ndarray:
-    """Flattened weight as fp32 values, zero padded to whole blocks, shape [nblk, 64]."""
+def _blocks_f32(w_bits: np.ndarray, block: int = BLOCK) -> np.ndarray:
+    """Flattened weight as fp32 values, zero padded to whole blocks, shape [nblk, block]."""
     flat = bf16_to_f32(np.ravel(w_bits))
-    nblk = num_blocks(flat.size)
-    out = np.zeros(nblk * BLOCK, dtype=np.float32)
+    nblk = num_blocks(flat.size, block)
+    out = np.zeros(nblk * block, dtype=np.float32)
     out[: flat.size] = flat
-    return out.reshape(nblk, BLOCK)
+    return out.reshape(nblk, block)
 
 
-def blockwise_absmax(w_bits: np.ndarray) -> np.ndarray:
-    """Largest magnitude of each 64-block (padding is zero so it never wins); reading R4 applied."""
-    a = np.abs(_blocks_f32(w_bits)).max(axis=1)
+def blockwise_absmax(w_bits: np.ndarray, block: int = BLOCK) -> np.ndarray:
+    """Largest magnitude of each block (padding is zero so it never wins); reading R4 applied."""
+    a = np.abs(_blocks_f32(w_bits, block)).max(axis=1)
     a[a < np.float32(FP32_MIN_NORMAL)] = 0.0
     return a.astype(np.float32)
 
@@ -212,15 +226,16 @@ def normalize_blocks(blocks: np.ndarray, absmax: np.ndarray) -> np.ndarray:
     return x
 
 
-def nf4_codes(w_bits: np.ndarray, absmax: np.ndarray | None = None, levels: np.ndarray | None = None) -> np.ndarray:
+def nf4_codes(w_bits: np.ndarray, absmax: np.ndarray | None = None, levels: np.ndarray | None = None,
+              block: int = BLOCK) -> np.ndarray:
     """Unpacked 4-bit codes (one uint8 per element, padded to whole blocks); NF4 unless
     another table is given."""
     lv = nf4_levels() if levels is None else levels
-    blocks = _blocks_f32(w_bits)
+    blocks = _blocks_f32(w_bits, block)
     if absmax is None:
-        absmax = blockwise_absmax(w_bits)
+        absmax = blockwise_absmax(w_bits, block)
     codes = np.empty(blocks.shape, dtype=np.uint8)
-    rows_per_chunk = max(1, _CHUNK // BLOCK)
+    rows_per_chunk = max(1, _CHUNK // block)
     for s in range(0, blocks.shape[0], rows_per_chunk):
         x = normalize_blocks(blocks[s:s + rows_per_chunk], absmax[s:s + rows_per_chunk])
         codes[s:s + rows_per_chunk] = nearest_level(x, lv).reshape(x.shape)
@@ -229,14 +244,14 @@ def nf4_codes(w_bits: np.ndarray, absmax: np.ndarray | None = None, levels: np.n
 
 
 def codes_for_blocks(w_bits: np.ndarray, absmax: np.ndarray, block_ids: np.ndarray,
-                     levels: np.ndarray | None = None) -> np.ndarray:
-    """Unpacked codes [len(block_ids), 64] of selected blocks only (for sampled checks at full size)."""
+                     levels: np.ndarray | None = None, block: int = BLOCK) -> np.ndarray:
+    """Unpacked codes [len(block_ids), block] of selected blocks only (for sampled checks at full size)."""
     lv = nf4_levels() if levels is None else levels
     flat = np.ravel(w_bits)
     block_ids = np.asarray(block_ids, dtype=np.int64)
-    blocks = np.zeros((block_ids.size, BLOCK), dtype=np.float32)
+    blocks = np.zeros((block_ids.size, block), dtype=np.float32)
     for i, b in enumerate(block_ids):
-        seg = bf16_to_f32(flat[b * BLOCK:(b + 1) * BLOCK])
+        seg = bf16_to_f32(flat[b * block:(b + 1) * block])
         blocks[i, : seg.size] = seg
     a = absmax[block_ids]
     codes = nearest_level(normalize_blocks(blocks, a), lv).reshape(blocks.shape)
@@ -244,11 +259,10 @@ def codes_for_blocks(w_bits: np.ndarray, absmax: np.ndarray, block_ids: np.ndarr
     return codes
 
 
-def pack_nibbles(codes: np.ndarray, numel: int, pad_code: int = ZERO_CODE) -> np.ndarray:
-    """Codes -> 32 bytes per 64-block in the layout of reading R6; returns nblk*32 bytes.
-    Positions past numel hold pad_code (the table's zero; 7 for NF4)."""
-    nblk = num_blocks(numel)
-    c = np.full(nblk * BLOCK, pad_code, dtype=np.uint8)
+def pack_nibbles(codes: np.ndarray, numel: int, pad_code: int = ZERO_CODE, block: int = BLOCK) -> np.ndarray:
+    """Codes -> 32 bytes per 64 elements in the layout of reading R6, for code_elems(numel,
+    block) elements.  Positions past numel hold pad_code (the table's zero; 7 for NF4)."""
+    c = np.full(code_elems(numel, block), pad_code, dtype=np.uint8)
     c[:numel] = np.ravel(codes)[:numel]
     g = c.reshape(-1, 8)                                   # one row per 8-element group
     return (g[:, 0:4] | (g[:, 4:8] << 4)).astype(np.uint8).reshape(-1)
@@ -343,15 +357,16 @@ def block_scales_dq(c2: np.ndarray, c1: np.ndarray, mu: np.float32) -> np.ndarra
 # ----------------------------------------------------------------------------------------------
 # Whole-tensor quantize / dequantize
 # ----------------------------------------------------------------------------------------------
-def quantize(w_bits: np.ndarray, double_quant: bool = True, codebook: str = "nf4") -> dict:
+def quantize(w_bits: np.ndarray, double_quant: bool = True, codebook: str = "nf4", block: int = BLOCK) -> dict:
     """Quantize a bf16 weight (any shape; flattened row-major) to 4-bit codes of a codebook
-    (NF4 by default) with optional double quant."""
+    (NF4 by default) in blocks of `block` weights (64 by default), with optional double quant."""
+    assert block in BLOCKS
     numel = int(np.asarray(w_bits).size)
     lv = codebook_levels(codebook)
-    absmax = blockwise_absmax(w_bits)
-    codes = nf4_codes(w_bits, absmax, lv)
-    q = {"numel": numel, "codes": pack_nibbles(codes, numel, zero_code(lv)), "absmax_true": absmax,
-         "double_quant": bool(double_quant), "codebook": codebook}
+    absmax = blockwise_absmax(w_bits, block)
+    codes = nf4_codes(w_bits, absmax, lv, block)
+    q = {"numel": numel, "codes": pack_nibbles(codes, numel, zero_code(lv), block), "absmax_true": absmax,
+         "double_quant": bool(double_quant), "codebook": codebook, "block": block}
     if double_quant:
         c2, c1, mu = double_quantize(absmax)
         q.update(c2=c2, c1=c1, mu=mu, scales=block_scales_dq(c2, c1, mu))
@@ -360,12 +375,13 @@ def quantize(w_bits: np.ndarray, double_quant: bool = True, codebook: str = "nf4
     return q
 
 
-def dequantize_codes(codes_unpacked: np.ndarray, scales: np.ndarray, levels: np.ndarray | None = None) -> np.ndarray:
+def dequantize_codes(codes_unpacked: np.ndarray, scales: np.ndarray, levels: np.ndarray | None = None,
+                     block: int = BLOCK) -> np.ndarray:
     """Outer dequant: bf16_RNE(fl32(level[code] * s')) per element (reading R12); NF4
     levels unless another table is given."""
     lv = nf4_levels() if levels is None else levels
     c = np.asarray(codes_unpacked, dtype=np.uint8).ravel()
-    blk = np.arange(c.size) // BLOCK
+    blk = np.arange(c.size) // block
     out = np.empty(c.size, dtype=np.uint16)
     for s in range(0, c.size, _CHUNK):
         prod = (lv[c[s:s + _CHUNK]] * scales[blk[s:s + _CHUNK]]).astype(np.float32)
@@ -376,22 +392,24 @@ def dequantize_codes(codes_unpacked: np.ndarray, scales: np.ndarray, levels: np.
 def dequantize(q: dict, shape=None) -> np.ndarray:
     """doubleDequant of a quantized tensor -> bf16 bit patterns (flattened, or reshaped)."""
     numel = q["numel"]
-    out = dequantize_codes(unpack_nibbles(q["codes"], numel), q["scales"], codebook_levels(q.get("codebook", "nf4")))
+    out = dequantize_codes(unpack_nibbles(q["codes"], numel), q["scales"], codebook_levels(q.get("codebook", "nf4")),
+                           q.get("block", BLOCK))
     return out.reshape(shape) if shape is not None else out
 
 
 # ----------------------------------------------------------------------------------------------
 # Storage accounting ([Explainer] "Double quantization" and "The QLoRA layer, end to end")
 # ----------------------------------------------------------------------------------------------
-def storage_bytes(numel: int, double_quant: bool = True) -> dict:
+def storage_bytes(numel: int, double_quant: bool = True, block: int = BLOCK) -> dict:
     """Bytes of each stored buffer: codes, block constants, second-level scales, mean."""
-    nblk = num_blocks(numel)
+    nblk = num_blocks(numel, block)
+    codes = code_elems(numel, block) // 2
     if double_quant:
-        return {"codes": 32 * nblk, "absmax": nblk, "c1": 4 * num_super(nblk), "mu": 4}
-    return {"codes": 32 * nblk, "absmax": 4 * nblk, "c1": 0, "mu": 0}
+        return {"codes": codes, "absmax": nblk, "c1": 4 * num_super(nblk), "mu": 4}
+    return {"codes": codes, "absmax": 4 * nblk, "c1": 0, "mu": 0}
 
 
-def constant_bits_per_param(numel: int, double_quant: bool = True) -> float:
+def constant_bits_per_param(numel: int, double_quant: bool = True, block: int = BLOCK) -> float:
     """Bits of quantization constants per weight (everything except the 4-bit codes)."""
-    b = storage_bytes(numel, double_quant)
+    b = storage_bytes(numel, double_quant, block)
     return 8.0 * (b["absmax"] + b["c1"] + b["mu"]) / numel
