@@ -27,7 +27,9 @@ Also reported:
   merge        -- adapter merge + requantize on the headline layer: times, and the
                   output error the requantization leaves;
   formats      -- quantization error (relative MSE of the dequantized weight) of the
-                  NF4, FP4 and Int4 tables on the headline weight shape;
+                  NF4, FP4 and Int4 tables on the headline weight shape, and for NF4
+                  blocks of 32, 64, 128, 256: error, constant bits per weight and the
+                  headline step time;
   mlp_7b, stack_65b -- forward+backward TFLOP/s over the 7B MLP pair (M = 4096)
                   and over the 65B layer stack (80 layers x 7 linears, M = 2048,
                   all 33 GB of NF4 weight resident), forward layer 0 first, then
@@ -407,20 +409,67 @@ def bench_layers(Q, workloads, torch, dev, cfg_idx, steps, warmup):
     return out
 
 
-def bench_formats(Q, workloads, torch, dev):
-    """Quantization error of the three 16-entry tables (NF4, FP4 = E2M1 / 6, Int4 = k / 7)
-    on the headline weight shape, with double quantization: relative mean squared error of
-    the dequantized bf16 weight, the synthetic stand-in for the pages' data-type comparison."""
+def bench_formats(Q, workloads, torch, dev, iters=20):
+    """Format variants on the headline weight shape, with double quantization.
+
+    codebooks: relative mean squared error of the dequantized bf16 weight for the three
+    16-entry tables (NF4, FP4 = E2M1 / 6, Int4 = k / 7), the synthetic stand-in for the
+    pages' data-type comparison.  block_sizes: for NF4 blocks of 32, 64, 128 and 256
+    weights, the same error (also with 0.1 % of the entries x20), the bits of constants per
+    weight from the library's buffer sizes, and the headline forward + backward step time
+    with that block size ("Double quantization": smaller blocks are more precise and pay
+    the per-block constant more often)."""
     W = workloads.device_normal_bf16(2500, (4096, 4096), 0.02)
-    w = W.float()
-    den = (w * w).mean().item()
-    out = {}
+    Wo = workloads.device_normal_bf16(2510, (4096, 4096), 0.02, outlier_p=0.001, mask_seed=2511)
+    w, wo = W.float(), Wo.float()
+    den, deno = (w * w).mean().item(), (wo * wo).mean().item()
+    out = {"codebooks": {}, "block_sizes": {}}
     for name, cb in Q.CODEBOOKS.items():
         q = Q.qlora_quantize_nf4(W, True, codebook=cb)
         d = Q.qlora_dequant(q).float()
-        out[name] = {"rel_mse": ((d - w) ** 2).mean().item() / den}
+        out["codebooks"][name] = {"rel_mse": ((d - w) ** 2).mean().item() / den}
         del q, d
-    out["order"] = " < ".join(sorted(Q.CODEBOOKS, key=lambda k: out[k]["rel_mse"]))
+    out["codebooks"]["order"] = " < ".join(sorted(Q.CODEBOOKS, key=lambda k: out["codebooks"][k]["rel_mse"]))
+
+    M, din, dout, r, s = 2048, 4096, 4096, 64, 0.25
+    A = workloads.device_normal_bf16(2520, (din, r), 0.02)
+    B = workloads.device_normal_bf16(2521, (r, dout), 0.02)
+    X = workloads.device_normal_bf16(2522, (M, din), 1.0)
+    dY = workloads.device_normal_bf16(2523, (M, dout), 1.0)
+    Y = torch.empty((M, dout), dtype=torch.bfloat16, device=dev)
+    T = torch.empty((M, r), dtype=torch.bfloat16, device=dev)
+    dX = torch.empty((M, din), dtype=torch.bfloat16, device=dev)
+    dA = torch.empty((din, r), dtype=torch.float32, device=dev)
+    dB = torch.empty((r, dout), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(Q.qlora_fwd_workspace(M, din, dout, r), Q.qlora_bwd_workspace(M, din, dout, r)),
+                     dtype=torch.uint8, device=dev)
+    flops = 4 * M * din * dout + 6 * M * r * (din + dout)
+    for block in (32, 64, 128, 256):
+        q = Q.qlora_quantize_nf4(W, True, block=block)
+        d = Q.qlora_dequant(q).float()
+        qo = Q.qlora_quantize_nf4(Wo, True, block=block)
+        do = Q.qlora_dequant(qo).float()
+        cb_, ab, c1b, mub = Q.qlora_nf4_sizes(dout, din, True, block)
+        rec = {"rel_mse": ((d - w) ** 2).mean().item() / den, "rel_mse_outliers": ((do - wo) ** 2).mean().item() / deno,
+               "constant_bits_per_weight": 8.0 * (ab + c1b + mub) / (din * dout)}
+
+        def step():
+            Q.qlora_linear_fwd(X, q, A, B, s, Y=Y, T_save=T, workspace=ws)
+            Q.qlora_linear_bwd(dY, X, T, q, A, B, s, dX=dX, dA=dA, dB=dB, workspace=ws)
+
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / iters
+        rec.update(step_ms=ms, step_TFLOPs=flops / (ms * 1e-3) / 1e12)
+        out["block_sizes"][str(block)] = rec
+        del q, d, qo, do
     torch.cuda.empty_cache()
     return out
 

@@ -63,15 +63,17 @@ class NF4Weight:
     rows: int
     cols: int
     double_quant: bool
-    codes: torch.Tensor      # uint8 [nblk*32]
+    codes: torch.Tensor      # uint8 [32 per 64 weights, padded to whole blocks]
     absmax: torch.Tensor     # uint8 [nblk] (double quant) or float32 [nblk]
     c1: torch.Tensor | None  # float32 [nsup]
     mu: torch.Tensor | None  # float32 [1]
     codebook: int = CODEBOOK_NF4
+    block: int = 64          # weights per constant: 32, 64, 128 or 256
 
     def desc(self) -> _lib.qlora_nf4:
-        return _lib.qlora_nf4(self.rows, self.cols, int(self.double_quant), int(self.codebook), self.codes.data_ptr(),
-                              self.absmax.data_ptr(), self.c1.data_ptr() if self.c1 is not None else None,
+        return _lib.qlora_nf4(self.rows, self.cols, int(self.double_quant), int(self.codebook), int(self.block), 0,
+                              self.codes.data_ptr(), self.absmax.data_ptr(),
+                              self.c1.data_ptr() if self.c1 is not None else None,
                               self.mu.data_ptr() if self.mu is not None else None)
 
     def nbytes(self) -> int:
@@ -94,14 +96,15 @@ def qlora_codebook_table(codebook: int = CODEBOOK_NF4):
     return list(lv), list(th)
 
 
-def qlora_nf4_sizes(rows: int, cols: int, double_quant: bool = True):
+def qlora_nf4_sizes(rows: int, cols: int, double_quant: bool = True, block: int = 64):
     out = [C.c_size_t() for _ in range(4)]
-    _check(lib().qlora_nf4_sizes(rows, cols, int(double_quant), *[C.byref(o) for o in out]), "qlora_nf4_sizes")
+    _check(lib().qlora_nf4_sizes(rows, cols, int(double_quant), int(block), *[C.byref(o) for o in out]),
+           "qlora_nf4_sizes")
     return tuple(o.value for o in out)
 
 
-def qlora_quantize_workspace(rows: int, cols: int, double_quant: bool = True) -> int:
-    return lib().qlora_quantize_workspace(rows, cols, int(double_quant))
+def qlora_quantize_workspace(rows: int, cols: int, double_quant: bool = True, block: int = 64) -> int:
+    return lib().qlora_quantize_workspace(rows, cols, int(double_quant), int(block))
 
 
 def qlora_fwd_workspace(M: int, d_in: int, d_out: int, r: int) -> int:
@@ -120,8 +123,9 @@ def _workspace(nbytes: int, device, ws):
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
-def nf4_alloc(rows: int, cols: int, double_quant: bool = True, device="cuda", codebook: int = CODEBOOK_NF4) -> NF4Weight:
-    cb, ab, c1b, mub = qlora_nf4_sizes(rows, cols, double_quant)
+def nf4_alloc(rows: int, cols: int, double_quant: bool = True, device="cuda", codebook: int = CODEBOOK_NF4,
+              block: int = 64) -> NF4Weight:
+    cb, ab, c1b, mub = qlora_nf4_sizes(rows, cols, double_quant, block)
     codes = torch.empty(cb, dtype=torch.uint8, device=device)
     if double_quant:
         absmax = torch.empty(ab, dtype=torch.uint8, device=device)
@@ -130,19 +134,20 @@ def nf4_alloc(rows: int, cols: int, double_quant: bool = True, device="cuda", co
     else:
         absmax = torch.empty(ab // 4, dtype=torch.float32, device=device)
         c1 = mu = None
-    return NF4Weight(rows, cols, double_quant, codes, absmax, c1, mu, codebook)
+    return NF4Weight(rows, cols, double_quant, codes, absmax, c1, mu, codebook, block)
 
 
 def qlora_quantize_nf4(W: torch.Tensor, double_quant: bool = True, out: NF4Weight | None = None,
-                       workspace: torch.Tensor | None = None, stream=None, codebook: int = CODEBOOK_NF4) -> NF4Weight:
+                       workspace: torch.Tensor | None = None, stream=None, codebook: int = CODEBOOK_NF4,
+                       block: int = 64) -> NF4Weight:
     """Quantize a bf16 [rows][cols] weight (any 2-D shape) to 4-bit codes of `codebook`
-    (NF4 by default) with blockwise absmax (+ double quantization).  With `out` given,
-    its own codebook is used."""
+    (NF4 by default) with one absmax per `block` weights (+ double quantization).  With
+    `out` given, its own codebook and block size are used."""
     _bf16(W, "W")
     rows, cols = (W.shape[0], W.shape[1]) if W.dim() == 2 else (1, W.numel())
     if out is None:
-        out = nf4_alloc(rows, cols, double_quant, W.device, codebook)
-    ws = _workspace(qlora_quantize_workspace(rows, cols, out.double_quant), W.device, workspace)
+        out = nf4_alloc(rows, cols, double_quant, W.device, codebook, block)
+    ws = _workspace(qlora_quantize_workspace(rows, cols, out.double_quant, out.block), W.device, workspace)
     d = out.desc()
     _check(lib().qlora_quantize_nf4(_ptr(W), rows, cols, C.byref(d), _ptr(ws),
                                     0 if ws is None else ws.numel(), _stream(stream)), "qlora_quantize_nf4")

@@ -24,6 +24,8 @@ class qlora_nf4(C.Structure):
         ("cols", C.c_int64),
         ("double_quant", C.c_int32),
         ("codebook", C.c_int32),
+        ("block_size", C.c_int32),
+        ("reserved", C.c_int32),
         ("codes", C.c_void_p),
         ("absmax", C.c_void_p),
         ("c1", C.c_void_p),
@@ -45,9 +47,9 @@ SIGNATURES = {
                                       C.c_void_p]),
     "qlora_adamw_step": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64, C.c_int64,
                                    C.c_float, C.c_float, C.c_float, C.c_float, C.c_float, C.c_void_p]),
-    "qlora_nf4_sizes": (C.c_int, [C.c_int64, C.c_int64, C.c_int32, C.POINTER(C.c_size_t), C.POINTER(C.c_size_t),
-                                  C.POINTER(C.c_size_t), C.POINTER(C.c_size_t)]),
-    "qlora_quantize_workspace": (C.c_size_t, [C.c_int64, C.c_int64, C.c_int32]),
+    "qlora_nf4_sizes": (C.c_int, [C.c_int64, C.c_int64, C.c_int32, C.c_int32, C.POINTER(C.c_size_t),
+                                  C.POINTER(C.c_size_t), C.POINTER(C.c_size_t), C.POINTER(C.c_size_t)]),
+    "qlora_quantize_workspace": (C.c_size_t, [C.c_int64, C.c_int64, C.c_int32, C.c_int32]),
     "qlora_fwd_workspace": (C.c_size_t, [C.c_int64, C.c_int64, C.c_int64, C.c_int32]),
     "qlora_bwd_workspace": (C.c_size_t, [C.c_int64, C.c_int64, C.c_int64, C.c_int32]),
     "qlora_quantize_nf4": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.POINTER(qlora_nf4), C.c_void_p, C.c_size_t,

@@ -86,6 +86,23 @@ struct Carve {
   }
 };
 
+// Weights per constant (0 in the descriptor means 64) and its log2; 0 for an unknown size.
+int block_of(int32_t b) { return b == 0 ? 64 : b; }
+int block_shift(int32_t b) {
+  switch (block_of(b)) {
+    case 32: return 5;
+    case 64: return 6;
+    case 128: return 7;
+    case 256: return 8;
+  }
+  return 0;
+}
+// elements the code buffer holds: whole blocks and whole 64-element chunks
+int64_t code_elems(int64_t numel, int block) {
+  const int64_t unit = std::max(block, 64);
+  return (numel + unit - 1) / unit * unit;
+}
+
 NF4View view_of(const qlora_nf4* w) {
   NF4View v;
   v.codes = w->codes;
@@ -94,6 +111,7 @@ NF4View view_of(const qlora_nf4* w) {
   v.mu = w->mu;
   v.dq = w->double_quant;
   v.cb = w->codebook;
+  v.bshift = block_shift(w->block_size);
   return v;
 }
 
@@ -106,6 +124,7 @@ qlora_status check_nf4(const qlora_nf4* w) {
   if (!w || !w->codes || !w->absmax) return QLORA_ERR_NULL;
   if (w->double_quant != 0 && w->double_quant != 1) return QLORA_ERR_UNSUPPORTED;
   if (w->codebook < 0 || w->codebook >= kNumCodebooks) return QLORA_ERR_UNSUPPORTED;
+  if (block_shift(w->block_size) == 0) return QLORA_ERR_UNSUPPORTED;
   if (w->double_quant && (!w->c1 || !w->mu)) return QLORA_ERR_NULL;
   if (w->rows < 1 || w->cols < 1 || w->rows >= kMaxDim || w->cols >= kMaxDim) return QLORA_ERR_SHAPE;
   if (!aligned16(w->codes) || !aligned4(w->absmax) || (w->c1 && !aligned4(w->c1)) || (w->mu && !aligned4(w->mu)))
@@ -117,7 +136,7 @@ qlora_status check_linear(int64_t M, const qlora_nf4* w, int32_t r) {
   qlora_status st = check_nf4(w);
   if (st != QLORA_OK) return st;
   if (M < 0 || M >= (int64_t(1) << 26)) return QLORA_ERR_SHAPE;
-  if (w->cols % 64 != 0 || w->rows % 8 != 0) return QLORA_ERR_SHAPE;
+  if (w->cols % 64 != 0 || w->cols % block_of(w->block_size) != 0 || w->rows % 8 != 0) return QLORA_ERR_SHAPE;
   if (w->rows > (int64_t(1) << 22) || w->cols > (int64_t(1) << 22)) return QLORA_ERR_SHAPE;
   if (r < 8 || r > 256 || r % 8 != 0) return QLORA_ERR_UNSUPPORTED;
   // the large-M kernels address each operand with 32-bit byte offsets
@@ -206,11 +225,11 @@ struct QuantWs {
   size_t bytes;
 };
 
-QuantWs quant_layout(void* base, int64_t numel) {
+QuantWs quant_layout(void* base, int64_t numel, int block) {
   Carve c(base);
   QuantWs ws;
   ws.hist = c.take<unsigned long long>(256 * kHistCopies);
-  ws.absmax = c.take<float>((size_t)((numel + 63) / 64));
+  ws.absmax = c.take<float>((size_t)((numel + block - 1) / block));
   ws.bytes = round_up(c.off, 256);
   return ws;
 }
@@ -247,23 +266,25 @@ qlora_status qlora_nf4_codebook(float levels[16], float thresholds[15]) {
   return QLORA_OK;
 }
 
-qlora_status qlora_nf4_sizes(int64_t rows, int64_t cols, int32_t dq, size_t* codes_bytes, size_t* absmax_bytes,
-                             size_t* c1_bytes, size_t* mu_bytes) {
+qlora_status qlora_nf4_sizes(int64_t rows, int64_t cols, int32_t dq, int32_t block_size, size_t* codes_bytes,
+                             size_t* absmax_bytes, size_t* c1_bytes, size_t* mu_bytes) {
   if (rows < 1 || cols < 1 || rows >= kMaxDim || cols >= kMaxDim) return QLORA_ERR_SHAPE;
   if (dq != 0 && dq != 1) return QLORA_ERR_UNSUPPORTED;
+  if (block_shift(block_size) == 0) return QLORA_ERR_UNSUPPORTED;
+  const int block = block_of(block_size);
   const int64_t numel = rows * cols;
-  const int64_t nblk = (numel + 63) / 64;
+  const int64_t nblk = (numel + block - 1) / block;
   const int64_t nsup = (nblk + 255) / 256;
-  if (codes_bytes) *codes_bytes = (size_t)nblk * 32;
+  if (codes_bytes) *codes_bytes = (size_t)code_elems(numel, block) / 2;
   if (absmax_bytes) *absmax_bytes = (size_t)nblk * (dq ? 1 : 4);
   if (c1_bytes) *c1_bytes = dq ? (size_t)nsup * 4 : 0;
   if (mu_bytes) *mu_bytes = dq ? 4 : 0;
   return QLORA_OK;
 }
 
-size_t qlora_quantize_workspace(int64_t rows, int64_t cols, int32_t dq) {
-  if (!dq || rows < 1 || cols < 1 || rows >= kMaxDim || cols >= kMaxDim) return 0;
-  return quant_layout(nullptr, rows * cols).bytes;
+size_t qlora_quantize_workspace(int64_t rows, int64_t cols, int32_t dq, int32_t block_size) {
+  if (!dq || rows < 1 || cols < 1 || rows >= kMaxDim || cols >= kMaxDim || block_shift(block_size) == 0) return 0;
+  return quant_layout(nullptr, rows * cols, block_of(block_size)).bytes;
 }
 
 size_t qlora_fwd_workspace(int64_t M, int64_t in, int64_t out, int32_t r) {
@@ -285,18 +306,20 @@ qlora_status qlora_quantize_nf4(const uint16_t* W, int64_t rows, int64_t cols, c
   if (st != QLORA_OK) return st;
   if (!aligned16(W)) return QLORA_ERR_ALIGN;
   const int64_t numel = rows * cols;
-  const int64_t nblk = (numel + 63) / 64;
+  const int block = block_of(out->block_size);
+  const int64_t nblk = (numel + block - 1) / block;
   if (out->double_quant) {
-    const QuantWs need = quant_layout(nullptr, numel);
+    const QuantWs need = quant_layout(nullptr, numel, block);
     if (!ws || ws_bytes < need.bytes) return QLORA_ERR_WORKSPACE;
     if (!aligned16(ws)) return QLORA_ERR_ALIGN;
-    const QuantWs q = quant_layout(ws, numel);
+    const QuantWs q = quant_layout(ws, numel, block);
     QL_HIP(launch_fill_u32(reinterpret_cast<uint32_t*>(q.hist), 512 * kHistCopies, 0u, stream));
-    QL_HIP(launch_quantize(W, numel, out->codebook, out->codes, q.absmax, q.hist, stream));
+    QL_HIP(launch_quantize(W, numel, out->codebook, block, out->codes, q.absmax, q.hist, stream));
     QL_HIP(launch_dq_mean(q.hist, nblk, out->mu, stream));
     QL_HIP(launch_dq_encode(q.absmax, nblk, out->mu, static_cast<uint8_t*>(out->absmax), out->c1, stream));
   } else {
-    QL_HIP(launch_quantize(W, numel, out->codebook, out->codes, static_cast<float*>(out->absmax), nullptr, stream));
+    QL_HIP(launch_quantize(W, numel, out->codebook, block, out->codes, static_cast<float*>(out->absmax), nullptr,
+                           stream));
   }
   return QLORA_OK;
 }

@@ -17,7 +17,7 @@ namespace qlora {
 
 constexpr int kBlock = 64;    // weights per NF4 block
 constexpr int kSuper = 256;   // block constants per second-level group
-constexpr int kBlockBytes = 32;
+constexpr int kBlockBytes = 32;   // code bytes per 64 weights (the code layout's chunk)
 constexpr int kHistCopies = 64;   // copies of the 256-bin exponent histogram (quantize workspace)
 
 // Passed by value to every kernel that encodes or decodes NF4 (lives in SGPRs /
@@ -30,12 +30,13 @@ struct NF4Table {
 
 // Describes a quantized weight inside kernels.
 struct NF4View {
-  const uint8_t* codes;   // nblk * 32 bytes
+  const uint8_t* codes;   // 32 bytes per 64 weights (code layout of qlora.h)
   const void* absmax;     // u8 E4M3 codes (dq) or fp32
   const float* c1;
   const float* mu;
   int32_t dq;
   int32_t cb;             // codebook: index of the 16-entry table the codes refer to
+  int32_t bshift;         // log2 of the block size (5..8): one constant per 2^bshift weights
 };
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

@@ -43,8 +43,10 @@ struct Stage {
   WRegs W;
 };
 
-// RAGGED: N % 64 != 0, the last stage's token columns past N are masked to zero
-template <bool DQ, bool RAGGED>
+// RAGGED: N % 64 != 0, the last stage's token columns past N are masked to zero.
+// BM: 0 for blocks of 64, 1 for 128 and 256 (a block spans two or four 64-column
+// halves of a row), 2 for 32 (two blocks per quad: each lane builds its own table).
+template <bool DQ, bool RAGGED, int BM>
 __global__ __launch_bounds__(NT) void k_bwd_dx_nf4_gemm(DxParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM_ELEMS];
   uint16_t* const sT[2] = {smem, smem + TILE_T};
@@ -73,20 +75,29 @@ __global__ __launch_bounds__(NT) void k_bwd_dx_nf4_gemm(DxParams p) {
   const float mu = dq ? *p.w.mu : 0.0f;
   const QuadLevels lev = quad_levels(p.tab);
 
+  const uint32_t bsh = (uint32_t)(p.w.bshift - 6);   // BM == 1: 64-chunks per block, log2
   auto load = [&](uint32_t it, Stage& S) {
     if constexpr (RAGGED)
       load_tokens_edge(S.T, ds, it * 64, N);
     else
       load_tokens(S.T, ds, it * 64);
-    const uint32_t blk = wblk0 + it * stage_blks;
+    const uint32_t blk = wblk0 + it * stage_blks;   // 64-element chunk of this thread's weights
     S.W.code = ld8(rC, blk * kBlockBytes + wq * 8);
+    // block of this thread's 16 weights
+    const uint32_t sb = BM == 0 ? blk : BM == 1 ? blk >> bsh : (blk << 1) + (uint32_t)(wq >> 1);
     if constexpr (dq) {
-      S.W.c2 = __builtin_amdgcn_raw_buffer_load_b8(rA, blk, 0, 0);
-      S.W.c1 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rC1, (blk >> 8) * 4, 0, 0));
+      S.W.c2 = __builtin_amdgcn_raw_buffer_load_b8(rA, sb, 0, 0);
+      S.W.c1 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rC1, (sb >> 8) * 4, 0, 0));
     } else {
-      S.W.c2 = __builtin_amdgcn_raw_buffer_load_b32(rA, blk * 4, 0, 0);
+      S.W.c2 = __builtin_amdgcn_raw_buffer_load_b32(rA, sb * 4, 0, 0);
       S.W.c1 = 0.0f;
     }
+  };
+  auto planes = [&](float scale) -> Planes {
+    if constexpr (BM == 2)
+      return make_planes(p.tab, scale);
+    else
+      return quad_planes(lev, scale);
   };
 
   auto scale_of = [&](const Stage& S) -> float {
@@ -108,7 +119,7 @@ __global__ __launch_bounds__(NT) void k_bwd_dx_nf4_gemm(DxParams p) {
     mma_group(acc, Fa, 1);
     store_tokens_part(S.T, sT[sb], 2);
     store_tokens_part(S.T, sT[sb], 3);
-    const Planes pl = quad_planes(lev, scale);
+    const Planes pl = planes(scale);
     mma_group(acc, Fb, 0);
     put(pl, S.W.code.x, 0, sb);
     mma_group(acc, Fb, 1);
@@ -119,7 +130,7 @@ __global__ __launch_bounds__(NT) void k_bwd_dx_nf4_gemm(DxParams p) {
   auto store_all = [&](const Stage& S, int sb) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) store_tokens_part(S.T, sT[sb], i);
-    const Planes pl = quad_planes(lev, scale_of(S));
+    const Planes pl = planes(scale_of(S));
     put(pl, S.W.code.x, 0, sb);
     put(pl, S.W.code.y, 1, sb);
   };
@@ -171,26 +182,37 @@ __global__ __launch_bounds__(NT) void k_bwd_dx_nf4_gemm(DxParams p) {
   if (combine_halves(acc, smem)) store_out(acc, p.dX, p.K, m0, p.M, k0, p.K);
 }
 
+// dispatch over the template flags (DQ, RAGGED, BM)
+template <int BM>
+void launch_dx_variant(bool dq, bool ragged, int bm, dim3 grid, dim3 block, const DxParams& p, hipStream_t s) {
+  if constexpr (BM < 2) {
+    if (bm != BM) return launch_dx_variant<BM + 1>(dq, ragged, bm, grid, block, p, s);
+  }
+  if (dq && !ragged)
+    hipLaunchKernelGGL((k_bwd_dx_nf4_gemm<true, false, BM>), grid, block, 0, s, p);
+  else if (dq)
+    hipLaunchKernelGGL((k_bwd_dx_nf4_gemm<true, true, BM>), grid, block, 0, s, p);
+  else if (!ragged)
+    hipLaunchKernelGGL((k_bwd_dx_nf4_gemm<false, false, BM>), grid, block, 0, s, p);
+  else
+    hipLaunchKernelGGL((k_bwd_dx_nf4_gemm<false, true, BM>), grid, block, 0, s, p);
+}
+
 }  // namespace
 
 hipError_t launch_dx_gemm(const uint16_t* dY, int64_t M, int64_t K, int64_t N, const NF4View& w,
                           const uint16_t* Gs, int64_t rp, const uint16_t* A, int64_t r, uint16_t* dX,
                           hipStream_t s) {
-  const uint64_t nblk = (uint64_t)N * K / 64;
-  DxParams p{dY, M, K, N, w, nblk * kBlockBytes, w.dq ? nblk : nblk * 4, w.dq ? ((nblk + 255) / 256) * 4 : 0,
+  // 64-element code chunks, and blocks (one constant each; in is a multiple of the block size)
+  const uint64_t nchunk = (uint64_t)N * K / 64, nblk = ((uint64_t)N * K) >> w.bshift;
+  DxParams p{dY, M, K, N, w, nchunk * kBlockBytes, w.dq ? nblk : nblk * 4, w.dq ? ((nblk + 255) / 256) * 4 : 0,
              Gs, rp, A, r, dX, nf4_table(w.cb)};
   const int64_t tiles = ((M + BT - 1) / BT) * ((K + BF - 1) / BF);
   ProfScope ps("k_bwd_dx_nf4_gemm", s);
   const dim3 grid((unsigned)tiles), block(NT);
   const bool ragged = (N % 64) != 0;
-  if (w.dq && !ragged)
-    hipLaunchKernelGGL((k_bwd_dx_nf4_gemm<true, false>), grid, block, 0, s, p);
-  else if (w.dq)
-    hipLaunchKernelGGL((k_bwd_dx_nf4_gemm<true, true>), grid, block, 0, s, p);
-  else if (!ragged)
-    hipLaunchKernelGGL((k_bwd_dx_nf4_gemm<false, false>), grid, block, 0, s, p);
-  else
-    hipLaunchKernelGGL((k_bwd_dx_nf4_gemm<false, true>), grid, block, 0, s, p);
+  const int bm = w.bshift == 6 ? 0 : w.bshift > 6 ? 1 : 2;
+  launch_dx_variant<0>(w.dq != 0, ragged, bm, grid, block, p, s);
   return hipGetLastError();
 }
 

@@ -44,7 +44,10 @@ struct Stage {
   WRegs W;
 };
 
-template <bool DQ>
+// BM: 0 for blocks of 64 (one block per row per stage), 1 for 128 and 256 (a block spans
+// 2 or 4 stages), 2 for 32 (two blocks per row per stage: the two halves of a quad use
+// different scales, so each lane builds the whole 16-entry table itself).
+template <bool DQ, int BM>
 __global__ __launch_bounds__(NT) void k_fwd_nf4_gemm(FwdParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM_ELEMS];
   uint16_t* const sT[2] = {smem, smem + TILE_T};
@@ -69,16 +72,35 @@ __global__ __launch_bounds__(NT) void k_fwd_nf4_gemm(FwdParams p) {
   const float mu = dq ? *p.w.mu : 0.0f;
   const QuadLevels lev = quad_levels(p.tab);
 
+  const uint32_t bsh = (uint32_t)(p.w.bshift - 6);   // BM == 1: 64-chunks per block, log2
   auto load = [&](uint32_t it, Stage& S) {
     load_tokens(S.T, xs, it * 64);
     S.W.code = ld8(rC, code_off, it * kBlockBytes);
-    if constexpr (dq) {
-      S.W.c2 = __builtin_amdgcn_raw_buffer_load_b8(rA, wblk0, it, 0);
-      S.W.c1 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rC1, ((wblk0 + it) >> 8) * 4, 0, 0));
+    if constexpr (BM == 0) {
+      if constexpr (dq) {
+        S.W.c2 = __builtin_amdgcn_raw_buffer_load_b8(rA, wblk0, it, 0);
+        S.W.c1 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rC1, ((wblk0 + it) >> 8) * 4, 0, 0));
+      } else {
+        S.W.c2 = __builtin_amdgcn_raw_buffer_load_b32(rA, wblk0 * 4, it * 4, 0);
+        S.W.c1 = 0.0f;
+      }
     } else {
-      S.W.c2 = __builtin_amdgcn_raw_buffer_load_b32(rA, wblk0 * 4, it * 4, 0);
-      S.W.c1 = 0.0f;
+      // block of this thread's 16 weights
+      const uint32_t sb = BM == 1 ? (wblk0 + it) >> bsh : ((wblk0 + it) << 1) + (uint32_t)(wq >> 1);
+      if constexpr (dq) {
+        S.W.c2 = __builtin_amdgcn_raw_buffer_load_b8(rA, sb, 0, 0);
+        S.W.c1 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rC1, (sb >> 8) * 4, 0, 0));
+      } else {
+        S.W.c2 = __builtin_amdgcn_raw_buffer_load_b32(rA, sb * 4, 0, 0);
+        S.W.c1 = 0.0f;
+      }
     }
+  };
+  auto planes = [&](float scale) -> Planes {
+    if constexpr (BM == 2)
+      return make_planes(p.tab, scale);
+    else
+      return quad_planes(lev, scale);
   };
 
   auto scale_of = [&](const Stage& S) -> float {
@@ -102,7 +124,7 @@ __global__ __launch_bounds__(NT) void k_fwd_nf4_gemm(FwdParams p) {
     mma_group(acc, Fa, 1);
     store_tokens_part(S.T, sT[sb], 2);
     store_tokens_part(S.T, sT[sb], 3);
-    const Planes pl = quad_planes(lev, scale);
+    const Planes pl = planes(scale);
     mma_group(acc, Fb, 0);
     put(pl, S.W.code.x, 0, sb);
     mma_group(acc, Fb, 1);
@@ -113,7 +135,7 @@ __global__ __launch_bounds__(NT) void k_fwd_nf4_gemm(FwdParams p) {
   auto store_all = [&](const Stage& S, int sb) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) store_tokens_part(S.T, sT[sb], i);
-    const Planes pl = quad_planes(lev, scale_of(S));
+    const Planes pl = planes(scale_of(S));
     put(pl, S.W.code.x, 0, sb);
     put(pl, S.W.code.y, 1, sb);
   };
@@ -171,15 +193,23 @@ __global__ __launch_bounds__(NT) void k_fwd_nf4_gemm(FwdParams p) {
 hipError_t launch_fwd_gemm(const uint16_t* X, int64_t M, int64_t K, int64_t N, const NF4View& w,
                            const uint16_t* Ts, int64_t rp, const uint16_t* B, int64_t r, uint16_t* Y,
                            hipStream_t s) {
-  const uint64_t nblk = (uint64_t)N * K / 64;
-  FwdParams p{X, M, K, N, w, nblk * kBlockBytes, w.dq ? nblk : nblk * 4, w.dq ? ((nblk + 255) / 256) * 4 : 0,
+  // 64-element code chunks, and blocks (one constant each; in is a multiple of the block size)
+  const uint64_t nchunk = (uint64_t)N * K / 64, nblk = ((uint64_t)N * K) >> w.bshift;
+  FwdParams p{X, M, K, N, w, nchunk * kBlockBytes, w.dq ? nblk : nblk * 4, w.dq ? ((nblk + 255) / 256) * 4 : 0,
               Ts, rp, B, r, Y, nf4_table(w.cb)};
   const int64_t tiles = ((M + BT - 1) / BT) * ((N + BF - 1) / BF);
+  const int bm = w.bshift == 6 ? 0 : w.bshift > 6 ? 1 : 2;
   ProfScope ps("k_fwd_nf4_gemm", s);
-  if (w.dq)
-    hipLaunchKernelGGL(k_fwd_nf4_gemm<true>, dim3((unsigned)tiles), dim3(NT), 0, s, p);
-  else
-    hipLaunchKernelGGL(k_fwd_nf4_gemm<false>, dim3((unsigned)tiles), dim3(NT), 0, s, p);
+  const dim3 grid((unsigned)tiles), block(NT);
+  if (w.dq) {
+    if (bm == 0) hipLaunchKernelGGL((k_fwd_nf4_gemm<true, 0>), grid, block, 0, s, p);
+    else if (bm == 1) hipLaunchKernelGGL((k_fwd_nf4_gemm<true, 1>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((k_fwd_nf4_gemm<true, 2>), grid, block, 0, s, p);
+  } else {
+    if (bm == 0) hipLaunchKernelGGL((k_fwd_nf4_gemm<false, 0>), grid, block, 0, s, p);
+    else if (bm == 1) hipLaunchKernelGGL((k_fwd_nf4_gemm<false, 1>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((k_fwd_nf4_gemm<false, 2>), grid, block, 0, s, p);
+  }
   return hipGetLastError();
 }
 

@@ -82,7 +82,9 @@ __device__ __forceinline__ int apos(int k, int q) {
 }
 
 // ---- weight workgroup: slice `slice` of the reduction, row groups [rg_beg, rg_end) ----
-template <bool DQ>
+// BM: 0 for blocks of 64 (one block per lane), 1 for 128 and 256 (neighbouring lanes share
+// a block), 2 for 32 (two blocks per lane: two constants and two tables).
+template <bool DQ, int BM>
 __device__ __forceinline__ void weight_group(const GemvParams& p, int bid, uint8_t* lds) {
   float4* const red = reinterpret_cast<float4*>(lds);          // [2][8][64]
   const int rranges = (int)p.rranges;
@@ -119,22 +121,37 @@ __device__ __forceinline__ void weight_group(const GemvParams& p, int bid, uint8
   const float mu = dq ? *p.w.mu : 0.0f;
 
   struct WStep {
-    uint4 c0, c1;     // the block's 32 code bytes
-    uint32_t c2;      // 8-bit block constant (double quant) or fp32 absmax bits
+    uint4 c0, c1;     // the 32 code bytes of the lane's 64 weights
+    uint32_t c2;      // 8-bit block constant (double quant) or fp32 absmax bits; for blocks
+                      // of 32 the two constants (two bytes, or the first fp32)
+    uint32_t c2b;     // blocks of 32 without double quant: the second fp32 absmax
     float c1f;        // group scale
   };
+  const uint32_t bsh = (uint32_t)(p.w.bshift - 6);   // BM == 1: 64-chunks per block, log2
   // row group rg_beg + i: row n = 16 (rg_beg + i) + row, block kbc of that row; rows past N
   // read past the end of the buffers and get zeros (their sums are not stored)
   auto load = [&](int i, WStep& S) {
     const uint32_t n = (uint32_t)((rg_beg + i) * RGR + row);
-    const uint32_t blk = n * (uint32_t)nkb + kbc;
+    const uint32_t blk = n * (uint32_t)nkb + kbc;   // 64-element chunk
     S.c0 = ld16(rC, blk * kBlockBytes);
     S.c1 = ld16(rC, blk * kBlockBytes + 16);
+    // first block of the chunk (blocks of 32: blocks 2 blk and 2 blk + 1, one group of 256)
+    const uint32_t sb = BM == 0 ? blk : BM == 1 ? blk >> bsh : blk << 1;
     if constexpr (dq) {
-      S.c2 = __builtin_amdgcn_raw_buffer_load_b8(rA, blk, 0, 0);
-      S.c1f = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rC1, (blk >> 8) * 4, 0, 0));
+      if constexpr (BM == 2)
+        S.c2 = __builtin_amdgcn_raw_buffer_load_b16(rA, sb, 0, 0);
+      else
+        S.c2 = __builtin_amdgcn_raw_buffer_load_b8(rA, sb, 0, 0);
+      S.c1f = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rC1, (sb >> 8) * 4, 0, 0));
+      S.c2b = 0;
     } else {
-      S.c2 = __builtin_amdgcn_raw_buffer_load_b32(rA, blk * 4, 0, 0);
+      if constexpr (BM == 2) {
+        S.c2 = __builtin_amdgcn_raw_buffer_load_b32(rA, sb * 4, 0, 0);
+        S.c2b = __builtin_amdgcn_raw_buffer_load_b32(rA, sb * 4 + 4, 0, 0);
+      } else {
+        S.c2 = __builtin_amdgcn_raw_buffer_load_b32(rA, sb * 4, 0, 0);
+        S.c2b = 0;
+      }
       S.c1f = 0.0f;
     }
   };
@@ -149,14 +166,22 @@ __device__ __forceinline__ void weight_group(const GemvParams& p, int bid, uint8
   // so waits for loads issued a moment earlier.
   auto step = [&](int i, const WStep& S) {
     __builtin_amdgcn_sched_barrier(0);
-    const float sc = dq ? __fadd_rn(__fmul_rn(e4m3_decode(S.c2), S.c1f), mu) : __uint_as_float(S.c2);
+    const float sc = dq ? __fadd_rn(__fmul_rn(e4m3_decode(S.c2 & 0xFFu), S.c1f), mu) : __uint_as_float(S.c2);
     u32x4 q0 = {S.c0.x, S.c0.y, S.c0.z, S.c0.w}, q1 = {S.c1.x, S.c1.y, S.c1.z, S.c1.w};
     asm volatile("" : "+v"(q0), "+v"(q1));
     const Planes pl = make_planes(p.tab, kvalid ? sc : 0.0f);
     const uint32_t cw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (BM == 2) {
+      // code words 0..3 hold the first block of 32, 4..7 the second
+      const float sc2 = dq ? __fadd_rn(__fmul_rn(e4m3_decode(S.c2 >> 8), S.c1f), mu) : __uint_as_float(S.c2b);
+      const Planes pl2 = make_planes(p.tab, kvalid ? sc2 : 0.0f);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) acc = mfma16(dequant8(pl, cw[c]), xr[c], acc);
+      for (int c = 0; c < 8; ++c) acc = mfma16(dequant8(c < 4 ? pl : pl2, cw[c]), xr[c], acc);
+    } else {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc = mfma16(dequant8(pl, cw[c]), xr[c], acc);
+    }
     float4* const buf = red + (i & 1) * 512;
     buf[wave * 64 + lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
     __syncthreads();
@@ -278,14 +303,14 @@ __device__ __forceinline__ void adapter_group(const GemvParams& p, int bid, uint
 
 // Workgroups [0, agroups * asplits) are adapter workgroups, the rest weight workgroups.
 // DQ: block constants are double-quantized (8-bit code, c1 per 256 blocks, mu).
-template <bool DQ>
+template <bool DQ, int BM>
 __global__ __launch_bounds__(GT) void k_fwd_nf4_gemv(GemvParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int n_adapter = (int)(p.agroups * p.asplits);
   if ((int)blockIdx.x < n_adapter)
     adapter_group(p, (int)blockIdx.x, lds);
   else
-    weight_group<DQ>(p, (int)blockIdx.x - n_adapter, lds);
+    weight_group<DQ, BM>(p, (int)blockIdx.x - n_adapter, lds);
 }
 
 // Y[m][n] = bf16( sum over slices of partial[slice][m][n] + sum_j Ts[m][j] B[j][n] ),
@@ -424,17 +449,25 @@ size_t gemv_partial_floats(const GemvPlan& pl, int64_t M) {
 
 hipError_t launch_gemv(const uint16_t* X, int64_t M, int64_t K, int64_t N, const NF4View& w, const uint16_t* A,
                        int64_t r, const GemvPlan& pl, float* partial, hipStream_t s) {
-  const uint64_t nblk = (uint64_t)N * K / 64;
-  GemvParams p{X, M, K, N, w, nblk * kBlockBytes, w.dq ? nblk : nblk * 4, w.dq ? ((nblk + 255) / 256) * 4 : 0,
+  // 64-element code chunks, and blocks (one constant each; in is a multiple of the block size)
+  const uint64_t nchunk = (uint64_t)N * K / 64, nblk = ((uint64_t)N * K) >> w.bshift;
+  GemvParams p{X, M, K, N, w, nchunk * kBlockBytes, w.dq ? nblk : nblk * 4, w.dq ? ((nblk + 255) / 256) * 4 : 0,
                A, r, partial, partial + pl.tpart, pl.npad, pl.agroups * GROWS, pl.splits, pl.rgroups,
                pl.rranges, pl.agroups, pl.asplits, nf4_table(w.cb)};
   const size_t lds = std::max(kLdsWeight, kLdsAdapter);
   ProfScope ps("k_fwd_nf4_gemv", s);
   const dim3 grid((unsigned)(pl.rranges * pl.splits + pl.agroups * pl.asplits));
-  if (w.dq)
-    hipLaunchKernelGGL(k_fwd_nf4_gemv<true>, grid, dim3(GT), lds, s, p);
-  else
-    hipLaunchKernelGGL(k_fwd_nf4_gemv<false>, grid, dim3(GT), lds, s, p);
+  const int bm = w.bshift == 6 ? 0 : w.bshift > 6 ? 1 : 2;
+  const dim3 block(GT);
+  if (w.dq) {
+    if (bm == 0) hipLaunchKernelGGL((k_fwd_nf4_gemv<true, 0>), grid, block, lds, s, p);
+    else if (bm == 1) hipLaunchKernelGGL((k_fwd_nf4_gemv<true, 1>), grid, block, lds, s, p);
+    else hipLaunchKernelGGL((k_fwd_nf4_gemv<true, 2>), grid, block, lds, s, p);
+  } else {
+    if (bm == 0) hipLaunchKernelGGL((k_fwd_nf4_gemv<false, 0>), grid, block, lds, s, p);
+    else if (bm == 1) hipLaunchKernelGGL((k_fwd_nf4_gemv<false, 1>), grid, block, lds, s, p);
+    else hipLaunchKernelGGL((k_fwd_nf4_gemv<false, 2>), grid, block, lds, s, p);
+  }
   return hipGetLastError();
 }
 

@@ -28,8 +28,8 @@ struct ProfScope {
 
 // ---- quantize / dequantize (quant.hip) --------------------------------------------------
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
-hipError_t launch_quantize(const uint16_t* W, int64_t numel, int codebook, uint8_t* codes, float* absmax_f32,
-                           unsigned long long* hist, hipStream_t s);
+hipError_t launch_quantize(const uint16_t* W, int64_t numel, int codebook, int block, uint8_t* codes,
+                           float* absmax_f32, unsigned long long* hist, hipStream_t s);
 hipError_t launch_dq_mean(const unsigned long long* hist, int64_t nblk, float* mu, hipStream_t s);
 hipError_t launch_dq_encode(const float* absmax_f32, int64_t nblk, const float* mu, uint8_t* c2, float* c1,
                             hipStream_t s);

@@ -8,8 +8,8 @@
 // Arithmetic per element: d = fp32 fused multiply-add chain over j = 0..r-1 of A[k][j] B[j][n]
 // (bf16 inputs, exact products), u = fl32(s d), W' = bf16_RNE(fl32(deq + u)) with deq the
 // bf16 dequantized weight ("doubleDequant").  One workgroup per 64 x 64 tile: rows of B and
-// of A^T for the tile staged in LDS, each thread 4 rows x 4 consecutive columns (one 64-block
-// per row: the 4 codes of a thread are the low or high nibbles of one code dword).
+// of A^T for the tile staged in LDS, each thread 4 rows x 4 consecutive columns (one 64-element
+// code chunk per row: the 4 codes of a thread are the low or high nibbles of one code dword).
 #include "common.h"
 #include "kernels.h"
 
@@ -61,9 +61,9 @@ __global__ __launch_bounds__(MT) void k_merge_adapter(NF4View w, int64_t N, int6
   for (int i = 0; i < 4; ++i) {
     const int64_t n = n0 + rn + i;
     if (n >= N) continue;
-    const int64_t blk = n * tiles_k + k0 / 64;
-    const float s = block_scale(w, blk);
-    const uint32_t cw = *reinterpret_cast<const uint32_t*>(w.codes + blk * kBlockBytes + g * 4);
+    const int64_t chunk = n * tiles_k + k0 / 64;                 // 64-element code chunk
+    const float s = block_scale(w, (n * K + k0 + ck) >> w.bshift);   // the 4 columns share a block
+    const uint32_t cw = *reinterpret_cast<const uint32_t*>(w.codes + chunk * kBlockBytes + g * 4);
     uint32_t o[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {

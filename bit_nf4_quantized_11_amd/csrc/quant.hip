@@ -3,7 +3,8 @@
 //
 // Sources ("QLoRA: Efficient Finetuning of Quantized LLMs"):
 //   "Quantize in blocks, not all at once" -- absmax scale per 64 contiguous weights,
-//       a value is normalized by multiplying it with c = 1/absmax;
+//       a value is normalized by multiplying it with c = 1/absmax ("Double quantization"
+//       weighs other block sizes: 32, 128 and 256 are supported as format variants);
 //   "NormalFloat: 4 bits for a bell curve" -- 16 levels, nearest level;
 //   "Double quantization" -- block constants, mean subtracted, as 8-bit floats in
 //       groups of 256 with one fp32 scale per group;
@@ -46,23 +47,27 @@ __device__ __forceinline__ uint32_t nf4_encode(float x, const Thr& t) {
   return ((uint32_t)b3 << 3) | ((uint32_t)b2 << 2) | ((uint32_t)b1 << 1) | (uint32_t)b0;
 }
 
-// Eight lanes per 64-block, eight consecutive weights per lane (one 16-byte load, one
+// L = block / 8 lanes per block, eight consecutive weights per lane (one 16-byte load, one
 // code dword).  Lane 0 of each group writes the fp32 block constant and, for double
 // quantization, adds it to a per-exponent histogram from which the exact sum of all
-// constants is rebuilt (integer adds: order-independent, hence deterministic).
+// constants is rebuilt (integer adds: order-independent, hence deterministic).  Blocks
+// from nblk up to ncode_blk (the code buffer's padding to whole 64-element chunks) get
+// zero codes and no constant.
+template <int L>
 __global__ __launch_bounds__(kThreads) void k_nf4_quantize(const uint16_t* __restrict__ W, int64_t numel,
-                                                           uint8_t* __restrict__ codes, float* __restrict__ absmax,
+                                                           int64_t ncode_blk, uint8_t* __restrict__ codes,
+                                                           float* __restrict__ absmax,
                                                            unsigned long long* __restrict__ hist, NF4Table tab) {
   __shared__ unsigned long long lhist[256];
   const bool dq = hist != nullptr;
   if (dq) lhist[threadIdx.x] = 0ull;
   __syncthreads();
-  const int sub = threadIdx.x & 7;
+  const int sub = threadIdx.x & (L - 1);
   const Thr thr = thr_regs(tab);
-  const int64_t nblk = (numel + 63) >> 6;
-  const int64_t stride = (int64_t)gridDim.x * (kThreads / 8);
-  for (int64_t blk = (int64_t)blockIdx.x * (kThreads / 8) + (threadIdx.x >> 3); blk < nblk; blk += stride) {
-    const int64_t e0 = blk * 64 + sub * 8;
+  const int64_t nblk = (numel + 8 * L - 1) / (8 * L);
+  const int64_t stride = (int64_t)gridDim.x * (kThreads / L);
+  for (int64_t blk = (int64_t)blockIdx.x * (kThreads / L) + (threadIdx.x / L); blk < ncode_blk; blk += stride) {
+    const int64_t e0 = blk * (8 * L) + sub * 8;
     uint32_t h[8];
     if (e0 + 8 <= numel) {
       const uint4 v = *reinterpret_cast<const uint4*>(W + e0);
@@ -76,9 +81,8 @@ __global__ __launch_bounds__(kThreads) void k_nf4_quantize(const uint16_t* __res
     uint32_t m = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) m = max(m, h[i] & 0x7FFFu);
-    m = max(m, (uint32_t)__shfl_xor((int)m, 1, 8));
-    m = max(m, (uint32_t)__shfl_xor((int)m, 2, 8));
-    m = max(m, (uint32_t)__shfl_xor((int)m, 4, 8));
+#pragma unroll
+    for (int off = 1; off < L; off <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, L));
     if (m < 0x0080u) m = 0;   // below the smallest normal: a zero block
     const float a = bf16_to_f32(m);
     // correctly rounded fp32 reciprocal (a float64 quotient rounded to fp32 is exact-rounded)
@@ -89,8 +93,8 @@ __global__ __launch_bounds__(kThreads) void k_nf4_quantize(const uint16_t* __res
     uint32_t packed = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) packed |= (c[i] | (c[i + 4] << 4)) << (8 * i);
-    *reinterpret_cast<uint32_t*>(codes + blk * kBlockBytes + sub * 4) = packed;
-    if (sub == 0) {
+    *reinterpret_cast<uint32_t*>(codes + (e0 >> 1)) = packed;
+    if (sub == 0 && blk < nblk) {
       absmax[blk] = a;
       if (dq && m) atomicAdd(&lhist[m >> 7], (unsigned long long)((m & 0x7Fu) | 0x80u));
     }
@@ -203,7 +207,7 @@ __global__ __launch_bounds__(kThreads) void k_dq_encode(const float* __restrict_
   }
 }
 
-// doubleDequant of a whole tensor: one thread per group of 8 weights.
+// doubleDequant of a whole tensor: one thread per group of 8 weights (4 code bytes).
 __global__ __launch_bounds__(kThreads) void k_nf4_dequant(NF4View w, int64_t numel, uint16_t* __restrict__ out,
                                                           NF4Table tab) {
   __shared__ float lv[16];
@@ -211,9 +215,9 @@ __global__ __launch_bounds__(kThreads) void k_nf4_dequant(NF4View w, int64_t num
   __syncthreads();
   const int64_t ngroups = (numel + 7) >> 3;
   for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < ngroups; g += (int64_t)gridDim.x * kThreads) {
-    const int64_t blk = g >> 3;
+    const int64_t blk = (g * 8) >> w.bshift;
     const float s = block_scale(w, blk);
-    const uint32_t cw = *reinterpret_cast<const uint32_t*>(w.codes + blk * kBlockBytes + (g & 7) * 4);
+    const uint32_t cw = *reinterpret_cast<const uint32_t*>(w.codes + g * 4);
     uint32_t v[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -263,12 +267,25 @@ hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_quantize(const uint16_t* W, int64_t numel, int codebook, uint8_t* codes, float* absmax_f32,
-                           unsigned long long* hist, hipStream_t s) {
-  const int64_t nblk = (numel + 63) / 64;
+hipError_t launch_quantize(const uint16_t* W, int64_t numel, int codebook, int block, uint8_t* codes,
+                           float* absmax_f32, unsigned long long* hist, hipStream_t s) {
+  const int64_t unit = block > 64 ? block : 64;   // the code buffer holds whole blocks and 64-chunks
+  const int64_t ncode_blk = (numel + unit - 1) / unit * (unit / block);
+  const unsigned grid = grid_for(ncode_blk, kThreads / (block / 8), 2048);
+  const NF4Table tab = nf4_table(codebook);
   ProfScope ps("k_nf4_quantize", s);
-  hipLaunchKernelGGL(k_nf4_quantize, dim3(grid_for(nblk, kThreads / 8, 2048)), dim3(kThreads), 0, s, W, numel,
-                     codes, absmax_f32, hist, nf4_table(codebook));
+  if (block == 32)
+    hipLaunchKernelGGL(k_nf4_quantize<4>, dim3(grid), dim3(kThreads), 0, s, W, numel, ncode_blk, codes, absmax_f32,
+                       hist, tab);
+  else if (block == 64)
+    hipLaunchKernelGGL(k_nf4_quantize<8>, dim3(grid), dim3(kThreads), 0, s, W, numel, ncode_blk, codes, absmax_f32,
+                       hist, tab);
+  else if (block == 128)
+    hipLaunchKernelGGL(k_nf4_quantize<16>, dim3(grid), dim3(kThreads), 0, s, W, numel, ncode_blk, codes, absmax_f32,
+                       hist, tab);
+  else
+    hipLaunchKernelGGL(k_nf4_quantize<32>, dim3(grid), dim3(kThreads), 0, s, W, numel, ncode_blk, codes, absmax_f32,
+                       hist, tab);
   return hipGetLastError();
 }
 

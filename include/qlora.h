@@ -51,16 +51,21 @@ typedef enum {
   QLORA_ERR_HIP = 6          /* a HIP runtime call or kernel launch failed                    */
 } qlora_status;
 
-/* Quantized weight: caller-owned views of device buffers.
- *   codes  : 32 * nblk bytes.  The flattened row-major weight is cut into blocks
- *            of 64, each stored whole in 32 bytes; inside a block the group of 8
- *            elements 8g..8g+7 sits in bytes 4g..4g+3, and byte i of a group holds
- *            element i in bits 3..0 and element i+4 in bits 7..4.  Positions past
- *            the end of the tensor hold the code of the table's exact zero (7 for
- *            NF4, 8 for FP4 and INT4).
+/* Quantized weight: caller-owned views of device buffers.  block_size B is the number
+ * of contiguous weights (of the flattened row-major tensor) that share one constant:
+ * 64 ("Quantize in blocks, not all at once"), or 32, 128 or 256 as format variants
+ * ("Double quantization" weighs precision against constant overhead); 0 means 64.
+ *   codes  : ncode / 2 bytes, ncode = rows*cols rounded up to a multiple of max(B, 64).
+ *            The group of 8 elements 8g..8g+7 sits in bytes 4g..4g+3, and byte i of a
+ *            group holds element i in bits 3..0 and element i+4 in bits 7..4 (so every
+ *            64 elements take 32 bytes whatever B).  Positions past the end of the
+ *            tensor hold the code of the table's exact zero (7 for NF4, 8 for FP4 and
+ *            INT4).
  *   absmax : double_quant = 1 -> nblk bytes, FP8 E4M3 code of (absmax_b - mu) / c1
+ *            (OCP e4m3fn: the quantizer writes magnitudes up to 448; the codes 0x7F
+ *            and 0xFF are NaN and give NaN weights if a caller stores them)
  *            double_quant = 0 -> nblk floats, the block absmax itself
- *            (nblk = ceil(rows*cols / 64))
+ *            (nblk = ceil(rows*cols / B))
  *   c1     : double_quant = 1 -> nsup floats, one scale per 256 blocks
  *            (nsup = ceil(nblk / 256)); unused (may be NULL) otherwise
  *   mu     : double_quant = 1 -> 1 float, the mean of all block absmax values;
@@ -74,6 +79,8 @@ typedef struct {
   int64_t cols;
   int32_t double_quant;
   int32_t codebook;      /* qlora_codebook: the 16-entry table the codes index (0 = NF4) */
+  int32_t block_size;    /* weights per constant: 32, 64, 128 or 256 (0 = 64)          */
+  int32_t reserved;      /* 0                                                            */
   uint8_t* codes;
   void* absmax;
   float* c1;
@@ -116,20 +123,21 @@ typedef enum { QLORA_CODEBOOK_NF4 = 0, QLORA_CODEBOOK_FP4 = 1, QLORA_CODEBOOK_IN
  * UNSUPPORTED for an unknown codebook.  Either pointer may be NULL.               */
 qlora_status qlora_codebook_table(int32_t codebook, float levels[16], float thresholds[15]);
 
-/* Host only.  Bytes of each buffer of a quantized [rows][cols] weight
- * ("Double quantization": 4-bit codes, 8-bit constants per 64, one fp32 per
- * 256 constants, one fp32 mean).  rows, cols >= 1.  Any output may be NULL.   */
-qlora_status qlora_nf4_sizes(int64_t rows, int64_t cols, int32_t double_quant, size_t* codes_bytes,
-                             size_t* absmax_bytes, size_t* c1_bytes, size_t* mu_bytes);
+/* Host only.  Bytes of each buffer of a quantized [rows][cols] weight with blocks of
+ * block_size (0 = 64) ("Double quantization": 4-bit codes, 8-bit constants per block,
+ * one fp32 per 256 constants, one fp32 mean).  rows, cols >= 1.  Any output may be
+ * NULL.  UNSUPPORTED for a block size other than 0, 32, 64, 128, 256.             */
+qlora_status qlora_nf4_sizes(int64_t rows, int64_t cols, int32_t double_quant, int32_t block_size,
+                             size_t* codes_bytes, size_t* absmax_bytes, size_t* c1_bytes, size_t* mu_bytes);
 
 /* Host only.  Workspace bytes each call needs (0 means none; pass ws = NULL). */
-size_t qlora_quantize_workspace(int64_t rows, int64_t cols, int32_t double_quant);
+size_t qlora_quantize_workspace(int64_t rows, int64_t cols, int32_t double_quant, int32_t block_size);
 size_t qlora_fwd_workspace(int64_t M, int64_t in_features, int64_t out_features, int32_t r);
 size_t qlora_bwd_workspace(int64_t M, int64_t in_features, int64_t out_features, int32_t r);
 
 /* Blockwise NF4 quantization of W [rows][cols] bf16 into `out` (whose rows,
  * cols, double_quant and buffers the caller sets; see qlora_nf4_sizes).
- * Per 64-block: a = max|w| (a below 2^-126 makes the block all zero codes with
+ * Per block of out->block_size: a = max|w| (a below 2^-126 makes the block all zero codes with
  * a = 0); x = fl32(w * fl32(1/a)); code = nearest level of out->codebook, ties to
  * the lower index ("Quantize in blocks, not all at once"; "NormalFloat").  With
  * double_quant: mu = fl32(S / nblk), S the exact sum of all a rounded once to
@@ -151,8 +159,9 @@ qlora_status qlora_dequant(const qlora_nf4* w, uint16_t* W_out, hipStream_t stre
  * to bf16 before its product with B.  If T_save is not NULL, bf16(T) is written
  * there [M][r] for the backward.  M >= 0; M = 0 is a no-op, and then the token
  * buffers X, Y and T_save may be NULL.
- * Requires: in % 64 == 0, out % 8 == 0, r % 8 == 0, 8 <= r <= 256; all pointers
- * 16-byte aligned; ws of qlora_fwd_workspace(M, in, out, r) bytes.            */
+ * Requires: in % 64 == 0 and in % block_size == 0 (blocks lie inside weight rows),
+ * out % 8 == 0, r % 8 == 0, 8 <= r <= 256; all pointers 16-byte aligned; ws of
+ * qlora_fwd_workspace(M, in, out, r) bytes.                                     */
 qlora_status qlora_linear_fwd(const uint16_t* X, int64_t M, const qlora_nf4* w, const uint16_t* A,
                               const uint16_t* B, int32_t r, float scale, uint16_t* Y, uint16_t* T_save,
                               void* ws, size_t ws_bytes, hipStream_t stream);
@@ -176,8 +185,8 @@ qlora_status qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, const uint1
  *   d = fp32 fused multiply-add chain over j = 0..r-1 of A[k][j] * B[j][n],
  * deq(W) the bf16 dequantized weight of the qlora_nf4 comment.  Quantize W_out again
  * with qlora_quantize_nf4 to get a merged 4-bit weight.  Same shape and alignment
- * rules as qlora_linear_fwd (in % 64 == 0, out % 8 == 0, r % 8 == 0, 8 <= r <= 256,
- * 16-byte aligned pointers).                                                        */
+ * rules as qlora_linear_fwd (in % 64 == 0, in % block_size == 0, out % 8 == 0, r % 8 == 0,
+ * 8 <= r <= 256, 16-byte aligned pointers).                                         */
 qlora_status qlora_merge_adapter(const qlora_nf4* w, const uint16_t* A, const uint16_t* B, int32_t r, float scale,
                                  uint16_t* W_out, hipStream_t stream);
 

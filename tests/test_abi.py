@@ -73,24 +73,30 @@ def test_library_codebook_tables_match_oracle(lib, cb, name):
     assert lib.qlora_codebook_table(-1, None, None) == 4
 
 
-@pytest.mark.parametrize("rows,cols,dq", [(4096, 4096, 1), (256, 256, 0), (3, 77, 1), (1, 1, 1), (22016, 8192, 1)])
-def test_sizes_match_oracle(lib, rows, cols, dq):
+@pytest.mark.parametrize("block", [0, 32, 64, 128, 256])
+@pytest.mark.parametrize("rows,cols,dq", [(4096, 4096, 1), (256, 256, 0), (3, 77, 1), (1, 1, 1), (22016, 8192, 1),
+                                          (5, 77, 0)])
+def test_sizes_match_oracle(lib, rows, cols, dq, block):
     out = [C.c_size_t() for _ in range(4)]
-    assert lib.qlora_nf4_sizes(rows, cols, dq, *[C.byref(o) for o in out]) == 0
-    ref = nf4.storage_bytes(rows * cols, bool(dq))
+    assert lib.qlora_nf4_sizes(rows, cols, dq, block, *[C.byref(o) for o in out]) == 0
+    ref = nf4.storage_bytes(rows * cols, bool(dq), block or 64)
     assert [o.value for o in out] == [ref["codes"], ref["absmax"], ref["c1"], ref["mu"]]
 
 
 def test_sizes_reject_bad_arguments(lib):
     z = C.c_size_t()
-    assert lib.qlora_nf4_sizes(0, 5, 1, C.byref(z), None, None, None) == 2
-    assert lib.qlora_nf4_sizes(5, -1, 1, None, None, None, None) == 2
-    assert lib.qlora_nf4_sizes(5, 5, 7, None, None, None, None) == 4
+    assert lib.qlora_nf4_sizes(0, 5, 1, 64, C.byref(z), None, None, None) == 2
+    assert lib.qlora_nf4_sizes(5, -1, 1, 64, None, None, None, None) == 2
+    assert lib.qlora_nf4_sizes(5, 5, 7, 64, None, None, None, None) == 4
+    for b in (16, 48, 512, -64):
+        assert lib.qlora_nf4_sizes(5, 5, 1, b, None, None, None, None) == 4
 
 
 def test_workspace_queries(lib):
-    assert lib.qlora_quantize_workspace(4096, 4096, 0) == 0
-    assert lib.qlora_quantize_workspace(4096, 4096, 1) >= 4 * 262144
+    assert lib.qlora_quantize_workspace(4096, 4096, 0, 64) == 0
+    assert lib.qlora_quantize_workspace(4096, 4096, 1, 64) >= 4 * 262144
+    assert lib.qlora_quantize_workspace(4096, 4096, 1, 32) >= 4 * 2 * 262144
+    assert lib.qlora_quantize_workspace(4096, 4096, 1, 48) == 0
     for M in (0, 1, 16, 17, 2048):
         f = lib.qlora_fwd_workspace(M, 4096, 4096, 64)
         b = lib.qlora_bwd_workspace(M, 4096, 4096, 64)
@@ -98,8 +104,8 @@ def test_workspace_queries(lib):
     assert lib.qlora_fwd_workspace(16, 4096, 4096, 300) == 0
 
 
-def _desc(rows=256, cols=256, dq=1, codes=0x10000, absmax=0x20000, c1=0x30000, mu=0x40000, cb=0):
-    return _lib.qlora_nf4(rows, cols, dq, cb, codes, absmax, c1, mu)
+def _desc(rows=256, cols=256, dq=1, codes=0x10000, absmax=0x20000, c1=0x30000, mu=0x40000, cb=0, block=0):
+    return _lib.qlora_nf4(rows, cols, dq, cb, block, 0, codes, absmax, c1, mu)
 
 
 def test_validation_errors_return_before_any_launch(lib):
@@ -125,6 +131,13 @@ def test_validation_errors_return_before_any_launch(lib):
     assert fwd(ok, 16, C.byref(_desc(dq=3)), ok, ok, 8, 2.0, ok, None, ws, big, None) == 4
     assert fwd(ok, 16, C.byref(_desc(cb=3)), ok, ok, 8, 2.0, ok, None, ws, big, None) == 4
     assert lib.qlora_quantize_nf4(ok, 256, 256, C.byref(_desc(cb=-1)), ws, big, None) == 4
+    # block sizes: unknown sizes are unsupported; a block must not straddle two weight rows
+    for b in (16, 96, 512):
+        assert fwd(ok, 16, C.byref(_desc(block=b)), ok, ok, 8, 2.0, ok, None, ws, big, None) == 4
+        assert lib.qlora_quantize_nf4(ok, 256, 256, C.byref(_desc(block=b)), ws, big, None) == 4
+        assert lib.qlora_dequant(C.byref(_desc(block=b)), ok, None) == 4
+    assert fwd(ok, 16, C.byref(_desc(cols=320, block=128)), ok, ok, 8, 2.0, ok, None, ws, big, None) == 2
+    assert fwd(ok, 16, C.byref(_desc(cols=384, block=256)), ok, ok, 8, 2.0, ok, None, ws, big, None) == 2
     # alignment
     assert fwd(C.c_void_p(0x100002), 16, C.byref(d), ok, ok, 8, 2.0, ok, None, ws, big, None) == 3
     assert fwd(ok, 16, C.byref(_desc(codes=0x10008)), ok, ok, 8, 2.0, ok, None, ws, big, None) == 3

@@ -13,16 +13,16 @@ from oracle import linear, nf4
 pytestmark = pytest.mark.gpu
 
 
-def _oracle_weight(w_u16, shape, dq=True, codebook="nf4"):
-    q = nf4.quantize(w_u16, double_quant=dq, codebook=codebook)
+def _oracle_weight(w_u16, shape, dq=True, codebook="nf4", block=64):
+    q = nf4.quantize(w_u16, double_quant=dq, codebook=codebook, block=block)
     return nf4.dequantize(q, shape)
 
 
-def _run(inp: workloads.LinearInputs, dq=True, save_T=True, need_dX=True, backward=True, codebook="nf4"):
+def _run(inp: workloads.LinearInputs, dq=True, save_T=True, need_dX=True, backward=True, codebook="nf4", block=64):
     require_gpu()
     lin = inp.spec
     W = dev_bf16(inp.W)
-    q = Q.qlora_quantize_nf4(W, double_quant=dq, codebook=Q.CODEBOOKS[codebook])
+    q = Q.qlora_quantize_nf4(W, double_quant=dq, codebook=Q.CODEBOOKS[codebook], block=block)
     X, A, B = dev_bf16(inp.X), dev_bf16(inp.A), dev_bf16(inp.B)
     Y, T = Q.qlora_linear_fwd(X, q, A, B, lin.scale, save_T=save_T)
     out = {"Y": Y, "T": T}
@@ -34,11 +34,11 @@ def _run(inp: workloads.LinearInputs, dq=True, save_T=True, need_dX=True, backwa
     return out
 
 
-def _check_full(inp, dq=True, save_T=True, need_dX=True, backward=True, label="", codebook="nf4"):
+def _check_full(inp, dq=True, save_T=True, need_dX=True, backward=True, label="", codebook="nf4", block=64):
     lin = inp.spec
-    log("linear", label, f"M={lin.M} in={lin.d_in} out={lin.d_out} r={lin.r} s={lin.scale}", codebook)
-    g = _run(inp, dq, save_T, need_dX, backward, codebook)
-    Wd = _oracle_weight(inp.W, (lin.d_out, lin.d_in), dq, codebook)
+    log("linear", label, f"M={lin.M} in={lin.d_in} out={lin.d_out} r={lin.r} s={lin.scale}", codebook, "block", block)
+    g = _run(inp, dq, save_T, need_dX, backward, codebook, block)
+    Wd = _oracle_weight(inp.W, (lin.d_out, lin.d_in), dq, codebook, block)
     y, t = linear.forward(inp.X, Wd, inp.A, inp.B, lin.scale)
     errs = {"Y": assert_close(host(g["Y"].float()), y, f"{label} Y")}
     if save_T:
@@ -107,6 +107,17 @@ def test_skinny_ragged_reduction_and_rows(dq):
     the end) and 40 output rows (a partial 16-row group), with and without double quant."""
     inp = workloads.custom_linear(3, 320, 40, 8, seed=11)
     _check_full(inp, dq=dq, label=f"skinny-ragged dq={dq}")
+
+
+@pytest.mark.parametrize("block", [32, 128, 256])
+@pytest.mark.parametrize("dq", [True, False])
+@pytest.mark.parametrize("M,din,dout,r", [(300, 512, 392, 16), (5, 1024, 520, 8), (16, 2304, 264, 24)])
+def test_block_sizes_linear(block, dq, M, din, dout, r):
+    """Forward and backward with blocks of 32, 128 and 256 weights: the large-M GEMMs
+    (ragged out for dX), the skinny path (a ragged reduction slice) and both constant
+    formats take the block size from the descriptor."""
+    inp = workloads.custom_linear(M, din, dout, r, seed=M + din + block)
+    _check_full(inp, dq=dq, label=f"block{block}{(M, din, dout, r)}", block=block)
 
 
 @pytest.mark.parametrize("codebook", ["fp4", "int4"])

@@ -19,18 +19,20 @@ def _bf16_ulp(x):
     return 2.0 ** (e - 7)
 
 
-@pytest.mark.parametrize("M,din,dout,r,dq,cb", [(4, 320, 264, 8, True, "nf4"), (4, 256, 128, 72, False, "nf4"),
-                                                (4, 512, 256, 256, True, "fp4"), (4, 4096, 4096, 64, True, "nf4")])
-def test_merge_matches_oracle(M, din, dout, r, dq, cb):
+@pytest.mark.parametrize("M,din,dout,r,dq,cb,block", [(4, 320, 264, 8, True, "nf4", 64), (4, 256, 128, 72, False, "nf4", 64),
+                                                      (4, 512, 256, 256, True, "fp4", 64),
+                                                      (4, 4096, 4096, 64, True, "nf4", 64),
+                                                      (4, 320, 264, 8, True, "nf4", 32), (4, 512, 256, 16, False, "nf4", 256)])
+def test_merge_matches_oracle(M, din, dout, r, dq, cb, block):
     require_gpu()
     inp = workloads.custom_linear(M, din, dout, r, seed=din + dout + r)
-    log("merge", din, dout, r, dq, cb)
-    w = Q.qlora_quantize_nf4(dev_bf16(inp.W), double_quant=dq, codebook=Q.CODEBOOKS[cb])
+    log("merge", din, dout, r, dq, cb, block)
+    w = Q.qlora_quantize_nf4(dev_bf16(inp.W), double_quant=dq, codebook=Q.CODEBOOKS[cb], block=block)
     s = 0.25
     Wm = Q.qlora_merge_adapter(w, dev_bf16(inp.A), dev_bf16(inp.B), s)
     torch.cuda.synchronize()
     got = host_u16(Wm)
-    Wd = nf4.dequantize(nf4.quantize(inp.W, double_quant=dq, codebook=cb), (dout, din))
+    Wd = nf4.dequantize(nf4.quantize(inp.W, double_quant=dq, codebook=cb, block=block), (dout, din))
     exact = linear.merge_adapter(Wd, inp.A, inp.B, s)
     g = nf4.bf16_to_f32(got).astype(np.float64)
     # one bf16 step of the result, plus the fp32 roundings of the adapter term and of the sum,
@@ -42,7 +44,7 @@ def test_merge_matches_oracle(M, din, dout, r, dq, cb):
     rne = nf4.f32_to_bf16(exact.astype(np.float32))
     assert np.mean(got == rne) > 0.999
     # requantize the merged weight: bit-exact with the oracle's quantizer on the same bf16 input
-    q2 = Q.qlora_quantize_nf4(Wm, double_quant=dq, codebook=Q.CODEBOOKS[cb])
+    q2 = Q.qlora_quantize_nf4(Wm, double_quant=dq, codebook=Q.CODEBOOKS[cb], block=block)
     torch.cuda.synchronize()
-    ref = nf4.quantize(got, double_quant=dq, codebook=cb)
+    ref = nf4.quantize(got, double_quant=dq, codebook=cb, block=block)
     assert np.array_equal(host(q2.codes), ref["codes"])

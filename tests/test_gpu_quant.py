@@ -12,19 +12,19 @@ from oracle import nf4
 pytestmark = pytest.mark.gpu
 
 
-def _gpu_quant(w_u16: np.ndarray, shape, dq: bool, codebook="nf4"):
+def _gpu_quant(w_u16: np.ndarray, shape, dq: bool, codebook="nf4", block=64):
     require_gpu()
     W = dev_bf16(w_u16.reshape(-1)).reshape(shape)
-    q = Q.qlora_quantize_nf4(W, double_quant=dq, codebook=Q.CODEBOOKS[codebook])
+    q = Q.qlora_quantize_nf4(W, double_quant=dq, codebook=Q.CODEBOOKS[codebook], block=block)
     deq = Q.qlora_dequant(q)
     torch.cuda.synchronize()
     return q, deq
 
 
-def _check(w_u16: np.ndarray, shape, dq: bool, label: str, codebook="nf4"):
-    log("quantize", label, shape, "dq" if dq else "no-dq", codebook)
-    q, deq = _gpu_quant(w_u16, shape, dq, codebook)
-    ref = nf4.quantize(w_u16, double_quant=dq, codebook=codebook)
+def _check(w_u16: np.ndarray, shape, dq: bool, label: str, codebook="nf4", block=64):
+    log("quantize", label, shape, "dq" if dq else "no-dq", codebook, "block", block)
+    q, deq = _gpu_quant(w_u16, shape, dq, codebook, block)
+    ref = nf4.quantize(w_u16, double_quant=dq, codebook=codebook, block=block)
     codes = host(q.codes)
     bad = np.flatnonzero(codes != ref["codes"])
     assert bad.size == 0, f"{label}: {bad.size} code bytes differ, first at byte {bad[:5]}"
@@ -47,6 +47,16 @@ def _check(w_u16: np.ndarray, shape, dq: bool, label: str, codebook="nf4"):
 def test_quantize_small_shapes(shape, dq):
     w = workloads.normal_bf16(7 + shape[0], shape, 0.02)
     _check(w, shape, dq, f"gauss{shape}")
+
+
+@pytest.mark.parametrize("block", [32, 128, 256])
+@pytest.mark.parametrize("shape,dq", [((256, 256), True), ((256, 256), False), ((3, 77), True), ((1, 96), False),
+                                      ((1, 64 * 256 * 3 + 5), True), ((4096, 4096), True)])
+def test_quantize_block_sizes(block, shape, dq):
+    """Blocks of 32, 128 and 256 weights through the same kernels: codes (padding to whole
+    blocks and 64-element chunks included), constants and dequantized weights bit-exact."""
+    w = workloads.normal_bf16(13 + shape[1] + block, shape, 0.02)
+    _check(w, shape, dq, f"block{block}{shape}", block=block)
 
 
 @pytest.mark.parametrize("codebook", ["fp4", "int4"])
