@@ -21,7 +21,8 @@ Also reported:
                   rotating 6 weight copies (> 512 MB) per shape;
   quantize     -- quantize + double-quantize of the headline weight (timed apart):
                   bytes moved (bf16 in, codes and constants out) over time;
-  adamw        -- one AdamW step on the adapters (fp32 state), GB/s against 8 TB/s;
+  adamw        -- one AdamW step on the adapters (fp32 state), GB/s against 8 TB/s, and
+                  with the state paged out to pinned host memory (GB/s over the link);
   comparators  -- the headline step on the unquantized bf16 weight and with the weight
                   dequantized into a buffer first (torch / hipBLASLt products), as context;
   merge        -- adapter merge + requantize on the headline layer: times, and the
@@ -591,7 +592,49 @@ def bench_adamw(Q, torch, dev, iters=10):
         out[name] = {"params": n, "us_per_step": us, "GBps": 30 * n / (us * 1e-6) / 1e9}
         del p, grad, m, v, pb
         torch.cuda.empty_cache()
+    out["host_state"] = bench_adamw_host_state(Q, torch, dev, iters)
     return out
+
+
+def bench_adamw_host_state(Q, torch, dev, iters, n=32 * 1024 * 1024):
+    """The same step with the fp32 master, m and v paged out to pinned host memory ("Paged
+    optimizers"): the kernel reads and writes them through their mapped device addresses
+    (hipHostGetDevicePointer), the gradient and the bf16 working copy stay in HBM.  24 bytes
+    per parameter cross the host link."""
+    import ctypes
+    with open("/proc/self/maps") as f:
+        paths = {line.split()[-1] for line in f if "libamdhip64.so" in line}
+    if len(paths) != 1:
+        return None
+    hip = ctypes.CDLL(paths.pop())
+    host = [torch.zeros(n, dtype=torch.float32).pin_memory() for _ in range(3)]
+    ptrs = []
+    for t in host:
+        d = ctypes.c_void_p()
+        if hip.hipHostGetDevicePointer(ctypes.byref(d), ctypes.c_void_p(t.data_ptr()), ctypes.c_uint(0)) != 0:
+            return None
+        ptrs.append(d)
+    grad = torch.full((n,), 1e-3, device=dev, dtype=torch.float32)
+    pb = torch.empty(n, device=dev, dtype=torch.bfloat16)
+    lib = Q.lib()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def step(t):
+        rc = lib.qlora_adamw_step(ptrs[0], ctypes.c_void_p(pb.data_ptr()), ctypes.c_void_p(grad.data_ptr()), ptrs[1],
+                                  ptrs[2], n, t, 2e-4, 0.9, 0.999, 1e-8, 0.01, stream)
+        if rc != 0:
+            raise RuntimeError(f"qlora_adamw_step: status {rc}")
+
+    step(1)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for t in range(2, 2 + iters):
+        step(t)
+    e1.record()
+    torch.cuda.synchronize()
+    us = 1e3 * e0.elapsed_time(e1) / iters
+    return {"params": n, "us_per_step": us, "host_link_GBps": 24 * n / (us * 1e-6) / 1e9}
 
 
 def cpu_baseline(M, din, dout, r, alpha, flops):

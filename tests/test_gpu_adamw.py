@@ -39,3 +39,61 @@ def test_adamw_steps_match_oracle(n, wd):
     assert np.max(np.abs(gm - rm)) <= 1e-6 * np.max(np.abs(rm))
     assert np.max(np.abs(gv - rv) / (np.abs(rv) + 1e-30)) <= 1e-5
     np.testing.assert_array_equal(host_u16(pb), nf4.f32_to_bf16(host(p)))
+
+
+def _hip_runtime():
+    """The HIP runtime this process already loaded (the one torch and the library use)."""
+    import ctypes
+    with open("/proc/self/maps") as f:
+        paths = {line.split()[-1] for line in f if "libamdhip64.so" in line}
+    assert len(paths) == 1, paths
+    return ctypes.CDLL(paths.pop())
+
+
+def _device_pointer(hip, t):
+    """Device address of a pinned host tensor, from hipHostGetDevicePointer (None if the
+    runtime does not map it)."""
+    import ctypes
+    d = ctypes.c_void_p()
+    rc = hip.hipHostGetDevicePointer(ctypes.byref(d), ctypes.c_void_p(t.data_ptr()), ctypes.c_uint(0))
+    return d.value if rc == 0 and d.value else None
+
+
+def test_adamw_state_in_host_memory():
+    """Optimizer state paged out to host memory ("Paged optimizers": the state lives in CPU
+    RAM and the GPU reaches it when the step runs): fp32 master, m and v in pinned host
+    memory, read and written by the kernel through their mapped device addresses, give
+    the same bits as the state in device memory."""
+    require_gpu()
+    import ctypes
+
+    hip = _hip_runtime()
+    n = 4096 * 64 + 5
+    rng = np.random.default_rng(11)
+    p0 = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    dev = torch.device("cuda", 0)
+    hp = torch.from_numpy(p0.copy()).pin_memory()
+    hm = torch.zeros(n, dtype=torch.float32).pin_memory()
+    hv = torch.zeros(n, dtype=torch.float32).pin_memory()
+    ptrs = [_device_pointer(hip, t) for t in (hp, hm, hv)]
+    if any(x is None for x in ptrs):
+        pytest.skip("pinned host memory is not mapped for the device")
+    dp = torch.from_numpy(p0.copy()).to(dev)
+    dm = torch.zeros(n, dtype=torch.float32, device=dev)
+    dv = torch.zeros(n, dtype=torch.float32, device=dev)
+    hb = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    db = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    lib = Q.lib()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for t in range(1, 4):
+        g = torch.from_numpy((rng.standard_normal(n) * 1e-3).astype(np.float32)).to(dev)
+        rc = lib.qlora_adamw_step(ctypes.c_void_p(ptrs[0]), ctypes.c_void_p(hb.data_ptr()),
+                                  ctypes.c_void_p(g.data_ptr()), ctypes.c_void_p(ptrs[1]), ctypes.c_void_p(ptrs[2]),
+                                  n, t, 2e-4, 0.9, 0.999, 1e-8, 0.01, stream)
+        assert rc == 0
+        Q.qlora_adamw_step(dp, g, dm, dv, t, 2e-4, 0.9, 0.999, 1e-8, 0.01, param_bf16=db)
+        torch.cuda.synchronize()
+    for a, b in ((hp, dp), (hm, dm), (hv, dv)):
+        assert torch.equal(a, b.cpu())
+    assert torch.equal(hb, db)
+
