@@ -24,7 +24,9 @@ Also reported:
   adamw        -- one AdamW step on the adapters (fp32 state), GB/s against 8 TB/s, and
                   with the state paged out to pinned host memory (GB/s over the link);
   comparators  -- the headline step on the unquantized bf16 weight and with the weight
-                  dequantized into a buffer first (torch / hipBLASLt products), as context;
+                  dequantized into a buffer first (torch / hipBLASLt products), as context,
+                  and measured ceilings: hipBLASLt's bf16 GEMM of the forward's shape (also
+                  in roofline.measured_ceiling) and torch's copy of 1 GiB;
   merge        -- adapter merge + requantize on the headline layer: times, and the
                   output error the requantization leaves;
   formats      -- quantization error (relative MSE of the dequantized weight) of the
@@ -252,6 +254,14 @@ def main():
         result["formats"] = bench_formats(Q, workloads, torch, dev)
         result["merge"] = bench_merge(Q, workloads, torch, dev)
         result["comparators"] = bench_comparators(Q, workloads, torch, dev, result["ms_per_step"])
+        gemm = result["comparators"]["ceilings"]["hipblaslt_bf16_gemm_2048x4096x4096"]
+        result["roofline"]["measured_ceiling"] = {
+            "what": "hipBLASLt bf16 GEMM of the same shape without dequantization (torch.matmul)",
+            "TFLOPs": gemm["TFLOPs"], "frac": result["roofline"]["achieved"] / gemm["TFLOPs"]}
+        if "gemv" in result:
+            cp = result["comparators"]["ceilings"]["device_copy_1GiB"]["GBps"]
+            result["gemv"]["measured_ceiling"] = {"what": "torch copy of 1 GiB, bytes read + written per second",
+                                                  "GBps": cp, "frac_max": result["gemv"]["weight_GBps_max"] / cp}
 
     if args.only in ("all", "adamw"):
         result["adamw"] = bench_adamw(Q, torch, dev)
@@ -518,7 +528,31 @@ def bench_comparators(Q, workloads, torch, dev, ms_qlora, iters=20):
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / iters
         out[name] = {"ms_per_step": ms, "qlora_step_over_this": ms_qlora / ms}
-    del W, A, B, X, dY, w, Wt, At, Bt, Xt, Wd
+
+    # measured ceilings: the plain bf16 GEMM of the forward's shape on hipBLASLt (no
+    # dequantization), and HBM streaming rates of torch's copy and sum over 1 GiB
+    def timed(fn, n):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return 1e3 * e0.elapsed_time(e1) / n   # us
+
+    us = timed(lambda: X @ Wt, 50)
+    big = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev).normal_()
+    dst = torch.empty_like(big)
+    us_copy = timed(lambda: dst.copy_(big), 10)
+    out["ceilings"] = {
+        "hipblaslt_bf16_gemm_2048x4096x4096": {"us": us, "TFLOPs": 2 * M * din * dout / (us * 1e-6) / 1e12},
+        "device_copy_1GiB": {"us": us_copy, "GBps": 2 * (1 << 30) / (us_copy * 1e-6) / 1e9,
+                             "note": "bytes read + written per second"},
+    }
+    del W, A, B, X, dY, w, Wt, At, Bt, Xt, Wd, big, dst
     torch.cuda.empty_cache()
     return out
 
