@@ -167,7 +167,7 @@ SmallGemm gemm_dB(const uint16_t* T, int64_t ldT, const uint16_t* dY, int64_t M,
   return SmallGemm{T, 1, ldT, dY, out, 1, r, out, M};
 }
 
-bool use_gemv(int64_t M) { return M <= 16; }
+bool use_gemv(int64_t M) { return M <= 64; }   // few tokens: the weight-streaming path
 
 LoraEpi epi_none() { return LoraEpi{nullptr, 0, 0.0f, nullptr, 0, 0.0f, nullptr, 0.0f}; }
 

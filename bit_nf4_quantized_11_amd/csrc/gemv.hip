@@ -1,4 +1,4 @@
-// Forward for few tokens (M <= 16), where the layer is bound by streaming the
+// Forward for few tokens (M <= 64), where the layer is bound by streaming the
 // packed weight from HBM ("QLoRA: Efficient Finetuning of Quantized LLMs",
 // section "The QLoRA layer, end to end": the weight is dequantized to bf16 on the
 // fly, used, and thrown away; y = x W + s (x L1) L2).
@@ -23,7 +23,10 @@
 // registers (8 x 16 bytes per lane) and the wave then streams row group after row group:
 // packed codes and block constants run four row groups ahead in a ring of registers.
 // After each row group the eight waves' 16 x 16 partial tiles meet in LDS (two buffers,
-// one barrier) and are summed in wave order.
+// one barrier) and are summed in wave order.  Batches of up to 64 tokens run as 2 or 4
+// groups of 16 (TG): each lane dequantizes its block once per row group and feeds it to
+// TG x 8 MFMAs, holding TG token operands in registers (one workgroup per CU then).
+// Adapter workgroups and the epilogue take one 16-token group each.
 #include "common.h"
 #include "gemm_core.h"
 #include "kernels.h"
@@ -45,12 +48,12 @@ constexpr int GROWS = 64;         // adapter columns per adapter workgroup
 constexpr int ACH = 64;           // rows of A per LDS chunk (8 KiB)
 constexpr int XAS = 72;           // X chunk row stride in the adapter workgroups (64 + 8 padding)
 constexpr int KA = 2048;          // rows of A per adapter slice
-constexpr int kSlotsPerCU = 2;    // resident workgroups per CU the grid is sized for
+constexpr int kSlotsPerCU = 2;    // resident workgroups per CU the grid is sized for (TG = 1)
 constexpr int RING = 4;           // row groups of packed weight in flight per wave
 
-// LDS: weight groups use two [8 waves][64 lanes] float4 tiles; adapter groups two A chunks,
-// two X chunks and the [4][64] float4 hand-over area of waves 4..7.
-constexpr size_t kLdsWeight = 2 * 8 * 64 * 16;
+// LDS: weight groups use two [TG][8 waves][64 lanes] float4 tiles; adapter groups two A
+// chunks, two X chunks and the [4][64] float4 hand-over area of waves 4..7.
+constexpr size_t kLdsWeight = 2 * 8 * 64 * 16;   // per token group
 constexpr size_t kLdsAdapter = 2 * ACH * 64 * 2 + 2 * 16 * XAS * 2 + 4 * 64 * 16;
 
 struct GemvParams {
@@ -69,6 +72,7 @@ struct GemvParams {
   int64_t rranges;      // weight workgroups per slice (contiguous ranges of row groups)
   int64_t agroups;      // adapter workgroups per adapter slice
   int asplits;
+  int ngr;              // 16-token groups
   NF4Table tab;
 };
 
@@ -84,9 +88,9 @@ __device__ __forceinline__ int apos(int k, int q) {
 // ---- weight workgroup: slice `slice` of the reduction, row groups [rg_beg, rg_end) ----
 // BM: 0 for blocks of 64 (one block per lane), 1 for 128 and 256 (neighbouring lanes share
 // a block), 2 for 32 (two blocks per lane: two constants and two tables).
-template <bool DQ, int BM>
+template <bool DQ, int BM, int TG>
 __device__ __forceinline__ void weight_group(const GemvParams& p, int bid, uint8_t* lds) {
-  float4* const red = reinterpret_cast<float4*>(lds);          // [2][8][64]
+  float4* const red = reinterpret_cast<float4*>(lds);          // [2][TG][8][64]
   const int rranges = (int)p.rranges;
   const int slice = bid / rranges, rr = bid - slice * rranges;
   const int64_t G = p.rgroups;
@@ -101,17 +105,22 @@ __device__ __forceinline__ void weight_group(const GemvParams& p, int bid, uint8
   const bool kvalid = kb < nkb;
   const uint32_t kbc = (uint32_t)(kvalid ? kb : nkb - 1);   // clamped; its scale is zero
 
-  // token operand of the 8 MFMAs: X[row][64 kb + 8c .. +7] (zero past M or past K)
-  u32x4 xr[8];
+  // token operand of the 8 MFMAs of token group tg: X[16 tg + row][64 kb + 8c .. +7] (zero
+  // past M or past K)
+  u32x4 xr[TG][8];
   {
     const rsrc_t rX = make_rsrc(p.X, (uint64_t)p.M * p.K * 2);
     const uint32_t xend = (uint32_t)(p.M * p.K * 2);
-    const uint32_t xo = (uint32_t)(row * (int)p.K + kb * 64) * 2;
-    const bool xin = row < M && kvalid;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const uint4 v = ld16(rX, xin ? xo + c * 16 : xend);
-      xr[c] = u32x4{v.x, v.y, v.z, v.w};
+    for (int tg = 0; tg < TG; ++tg) {
+      const int m = tg * 16 + row;
+      const uint32_t xo = (uint32_t)(m * (int)p.K + kb * 64) * 2;
+      const bool xin = m < M && kvalid;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const uint4 v = ld16(rX, xin ? xo + c * 16 : xend);
+        xr[tg][c] = u32x4{v.x, v.y, v.z, v.w};
+      }
     }
   }
   const rsrc_t rC = make_rsrc(p.w.codes, p.codes_bytes);
@@ -155,12 +164,12 @@ __device__ __forceinline__ void weight_group(const GemvParams& p, int bid, uint8
       S.c1f = 0.0f;
     }
   };
-  // reduction of the tiles: thread t < 256 sums element (row t % 16, token t / 16) of the
-  // eight waves' tiles, in wave order; acc[v] of lane l holds row 4 (l / 16) + v, token l % 16
-  const int rrow = t & 15, rtok = t >> 4;
-  const int roff = ((rrow >> 2) * 16 + (rtok & 15)) * 4 + (rrow & 3);
+  // reduction of the tiles: thread t sums element (row t % 16, token (t % 256) / 16) of the
+  // eight waves' tiles of token groups t / 256, t / 256 + 2, .., in wave order; acc[v] of
+  // lane l holds row 4 (l / 16) + v, token l % 16
+  const int rrow = t & 15, rtok = (t & 255) >> 4;
+  const int roff = ((rrow >> 2) * 16 + rtok) * 4 + (rrow & 3);
   float* const pout = p.partial + ((int64_t)slice * p.M + rtok) * p.npad + rrow;
-  const bool rstore = t < 256 && rtok < M;
   // The scheduling barriers and the empty asm keep each step's work inside its step: left
   // free, the compiler moves arithmetic on the next step's freshly loaded codes ahead and
   // so waits for loads issued a moment earlier.
@@ -171,27 +180,42 @@ __device__ __forceinline__ void weight_group(const GemvParams& p, int bid, uint8
     asm volatile("" : "+v"(q0), "+v"(q1));
     const Planes pl = make_planes(p.tab, kvalid ? sc : 0.0f);
     const uint32_t cw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc[TG];
+#pragma unroll
+    for (int tg = 0; tg < TG; ++tg) acc[tg] = f32x4{0.f, 0.f, 0.f, 0.f};
     if constexpr (BM == 2) {
       // code words 0..3 hold the first block of 32, 4..7 the second
       const float sc2 = dq ? __fadd_rn(__fmul_rn(e4m3_decode(S.c2 >> 8), S.c1f), mu) : __uint_as_float(S.c2b);
       const Planes pl2 = make_planes(p.tab, kvalid ? sc2 : 0.0f);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) acc = mfma16(dequant8(c < 4 ? pl : pl2, cw[c]), xr[c], acc);
+      for (int c = 0; c < 8; ++c) {
+        const u32x4 wv = dequant8(c < 4 ? pl : pl2, cw[c]);
+#pragma unroll
+        for (int tg = 0; tg < TG; ++tg) acc[tg] = mfma16(wv, xr[tg][c], acc[tg]);
+      }
     } else {
 #pragma unroll
-      for (int c = 0; c < 8; ++c) acc = mfma16(dequant8(pl, cw[c]), xr[c], acc);
+      for (int c = 0; c < 8; ++c) {
+        const u32x4 wv = dequant8(pl, cw[c]);
+#pragma unroll
+        for (int tg = 0; tg < TG; ++tg) acc[tg] = mfma16(wv, xr[tg][c], acc[tg]);
+      }
     }
-    float4* const buf = red + (i & 1) * 512;
-    buf[wave * 64 + lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    float4* const buf = red + (i & 1) * (512 * TG);
+#pragma unroll
+    for (int tg = 0; tg < TG; ++tg)
+      buf[tg * 512 + wave * 64 + lane] = make_float4(acc[tg][0], acc[tg][1], acc[tg][2], acc[tg][3]);
     __syncthreads();
     const int n = (rg_beg + i) * RGR + rrow;
-    if (rstore && n < N) {
-      const float* b = reinterpret_cast<const float*>(buf) + roff;
-      float sum = b[0];
 #pragma unroll
-      for (int w = 1; w < 8; ++w) sum = __fadd_rn(sum, b[w * 256]);
-      pout[(int64_t)(rg_beg + i) * RGR] = sum;
+    for (int tg = 0; tg < TG; ++tg) {
+      if ((t >> 8) == (tg & 1) && tg * 16 + rtok < M && n < N) {
+        const float* b = reinterpret_cast<const float*>(buf + tg * 512) + roff;
+        float sum = b[0];
+#pragma unroll
+        for (int w = 1; w < 8; ++w) sum = __fadd_rn(sum, b[w * 256]);
+        pout[(int64_t)tg * 16 * p.npad + (int64_t)(rg_beg + i) * RGR] = sum;
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -223,17 +247,20 @@ __device__ __forceinline__ void adapter_group(const GemvParams& p, int bid, uint
   uint16_t* const sXa = sAb + 2 * ACH * 64;                    // [2][16][XAS]
   float4* const sAcc = reinterpret_cast<float4*>(sXa + 2 * 16 * XAS);   // [4][64]
   const int nsp = p.asplits;
-  const int grp = bid / nsp;
-  const int split = bid - grp * nsp;
+  const int tgi = bid % p.ngr;                                 // this workgroup's 16-token group
+  const int rest = bid / p.ngr;
+  const int grp = rest / nsp;
+  const int split = rest - grp * nsp;
+  const int m0 = tgi * 16;
   const int kb_beg = split * (KA / 64);
   const int nkb = (int)(p.K / 64);
   const int nkb_s = min(nkb, kb_beg + KA / 64) - kb_beg;      // blocks (64-row chunks) in this slice
-  const int M = (int)p.M;
+  const int M = min((int)p.M - m0, 16);      // tokens of this group
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wq = wave & 3, par = wave >> 2;
   const int row = lane & 15, g = lane >> 4;
-  const int xrow = row < M ? row : row % M;   // token rows past M repeat real rows (outputs unused)
+  const int xrow = row < M ? row : row % M;   // token rows past the group repeat real rows (outputs unused)
   const rsrc_t rX = make_rsrc(p.X, (uint64_t)p.M * p.K * 2);
   const uint32_t xend = (uint32_t)(p.M * p.K * 2);
   const int j0 = grp * GROWS;
@@ -253,7 +280,8 @@ __device__ __forceinline__ void adapter_group(const GemvParams& p, int bid, uint
       const int c = cb + u;
       const int k = (kb_beg + c) * 64 + lr;
       va[u] = ld16(rAd, col_ok && c < nkb_s ? (uint32_t)((k * (int)p.r + j0 + lq * 8) * 2) : aend);
-      vx[u] = ld16(rX, xload && c < nkb_s ? (uint32_t)((xm * (int)p.K + (kb_beg + c) * 64 + lq * 8) * 2) : xend);
+      vx[u] = ld16(rX, xload && c < nkb_s ? (uint32_t)(((m0 + xm) * (int)p.K + (kb_beg + c) * 64 + lq * 8) * 2)
+                                         : xend);
     }
   };
   auto proc4 = [&](int cb, const uint4 (&va)[4], const uint4 (&vx)[4]) {
@@ -295,7 +323,7 @@ __device__ __forceinline__ void adapter_group(const GemvParams& p, int bid, uint
   if (!par && row < M) {
     const float4 o = sAcc[wq * 64 + lane];
     const int64_t n = (int64_t)grp * GROWS + wq * 16 + 4 * g;
-    float* dst = p.tpartial + ((int64_t)split * p.M + row) * p.rp + n;
+    float* dst = p.tpartial + ((int64_t)split * p.M + m0 + row) * p.rp + n;
     *reinterpret_cast<float4*>(dst) = make_float4(__fadd_rn(acc[0], o.x), __fadd_rn(acc[1], o.y),
                                                   __fadd_rn(acc[2], o.z), __fadd_rn(acc[3], o.w));
   }
@@ -303,20 +331,21 @@ __device__ __forceinline__ void adapter_group(const GemvParams& p, int bid, uint
 
 // Workgroups [0, agroups * asplits) are adapter workgroups, the rest weight workgroups.
 // DQ: block constants are double-quantized (8-bit code, c1 per 256 blocks, mu).
-template <bool DQ, int BM>
+template <bool DQ, int BM, int TG>
 __global__ __launch_bounds__(GT) void k_fwd_nf4_gemv(GemvParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  const int n_adapter = (int)(p.agroups * p.asplits);
+  const int n_adapter = (int)(p.agroups * p.asplits) * p.ngr;
   if ((int)blockIdx.x < n_adapter)
     adapter_group(p, (int)blockIdx.x, lds);
   else
-    weight_group<DQ, BM>(p, (int)blockIdx.x - n_adapter, lds);
+    weight_group<DQ, BM, TG>(p, (int)blockIdx.x - n_adapter, lds);
 }
 
 // Y[m][n] = bf16( sum over slices of partial[slice][m][n] + sum_j Ts[m][j] B[j][n] ),
 // Ts = bf16(s T), T = sum over adapter slices of tpartial[slice][m][j] (formed again by every
-// workgroup: M r values); block 0 also writes T_save = bf16(T).  A workgroup covers 64 columns;
-// thread t takes column t % 64 for the tokens m = t / 64 + 4 q.  The loads of the first 8
+// workgroup: 16 r values); column block 0 also writes T_save = bf16(T).  A workgroup covers
+// 64 columns of one 16-token group (blockIdx.y); thread t takes column t % 64 for the tokens
+// m = t / 64 + 4 q of the group.  The loads of the first 8
 // slices of both sums and of B are all issued before any of them is used, so the common case
 // waits for memory once; sums run in slice order.
 __global__ __launch_bounds__(256) void k_gemv_epilogue(const float* __restrict__ partial, int splits,
@@ -331,8 +360,14 @@ __global__ __launch_bounds__(256) void k_gemv_epilogue(const float* __restrict__
   const int c = t & 63, mq = t >> 6;
   const int64_t n = n0 + c;
   const int64_t nc = n < N ? n : N - 1;          // clamped column: every load stays inside the partials
-  const int mcap = (int)M - 1;
-  const int MR = (int)(M * rp);                  // T entries (at most 16 x 256)
+  const int64_t m0 = (int64_t)blockIdx.y * 16;   // first token of the group
+  const int Mg = (int)min<int64_t>(16, M - m0);  // tokens of the group
+  const int mcap = Mg - 1;
+  const int MR = (int)(Mg * rp);                 // T entries of the group (at most 16 x 256)
+  partial += m0 * npad;                          // row m of the group: partial[(sp M + m) npad + n]
+  tpartial += m0 * rp;                           // tpartial[sp M rp + m rp + j]
+  Y += m0 * N;
+  if (T_save) T_save += m0 * r;
 
   // weight partials of the first 8 slices (slice indices past the end repeat the last one, unused)
   float v[8][4];
@@ -363,7 +398,7 @@ __global__ __launch_bounds__(256) void k_gemv_epilogue(const float* __restrict__
       for (int u = 0; u < 8; ++u) {
         const int sp = min(s0 + u, asplits - 1);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) tv[u][e] = tpartial[(int64_t)sp * MR + min(e0 + e * 256 + t, MR - 1)];
+        for (int e = 0; e < 4; ++e) tv[u][e] = tpartial[(int64_t)sp * M * rp + min(e0 + e * 256 + t, MR - 1)];
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u)
@@ -419,7 +454,25 @@ __global__ __launch_bounds__(256) void k_gemv_epilogue(const float* __restrict__
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int m = mq + 4 * q;
-    if (m < M) Y[m * N + n] = (uint16_t)f32_to_bf16_bits(__fadd_rn(acc[q], lora[q]));
+    if (m < Mg) Y[m * N + n] = (uint16_t)f32_to_bf16_bits(__fadd_rn(acc[q], lora[q]));
+  }
+}
+
+// dispatch over the template flags (DQ, BM, TG)
+template <int TG>
+void launch_gemv_variant(bool dq, int bm, int tg, dim3 grid, size_t lds, const GemvParams& p, hipStream_t s) {
+  if constexpr (TG < 4) {
+    if (tg != TG) return launch_gemv_variant<TG * 2>(dq, bm, tg, grid, lds, p, s);
+  }
+  const dim3 block(GT);
+  if (dq) {
+    if (bm == 0) hipLaunchKernelGGL((k_fwd_nf4_gemv<true, 0, TG>), grid, block, lds, s, p);
+    else if (bm == 1) hipLaunchKernelGGL((k_fwd_nf4_gemv<true, 1, TG>), grid, block, lds, s, p);
+    else hipLaunchKernelGGL((k_fwd_nf4_gemv<true, 2, TG>), grid, block, lds, s, p);
+  } else {
+    if (bm == 0) hipLaunchKernelGGL((k_fwd_nf4_gemv<false, 0, TG>), grid, block, lds, s, p);
+    else if (bm == 1) hipLaunchKernelGGL((k_fwd_nf4_gemv<false, 1, TG>), grid, block, lds, s, p);
+    else hipLaunchKernelGGL((k_fwd_nf4_gemv<false, 2, TG>), grid, block, lds, s, p);
   }
 }
 
@@ -428,16 +481,18 @@ __global__ __launch_bounds__(256) void k_gemv_epilogue(const float* __restrict__
 // Weight slices of SLB blocks, each split into contiguous ranges of 16-row groups, and
 // adapter slices of KA rows of A.  The grid fills kSlotsPerCU workgroups per CU in one round.
 GemvPlan gemv_plan(int64_t M, int64_t K, int64_t N, int64_t rp) {
-  const int64_t slots = 256 * kSlotsPerCU;
   const int64_t nkb = K / 64;
   const int64_t Mm = std::max<int64_t>(M, 1);
   GemvPlan pl;
+  pl.ngr = (int)((Mm + 15) / 16);
+  pl.tg = pl.ngr == 1 ? 1 : pl.ngr == 2 ? 2 : 4;
+  const int64_t slots = 256 * (pl.tg == 1 ? kSlotsPerCU : 1);   // TG > 1: 256 VGPRs, one per CU
   pl.splits = (int)((nkb + SLB - 1) / SLB);
   pl.rgroups = (N + RGR - 1) / RGR;
   pl.npad = pl.rgroups * RGR;
   pl.agroups = rp / GROWS;
   pl.asplits = (int)((K + KA - 1) / KA);
-  const int64_t aw = pl.agroups * pl.asplits;
+  const int64_t aw = pl.agroups * pl.asplits * pl.ngr;
   pl.rranges = std::max<int64_t>(1, std::min<int64_t>(pl.rgroups, (slots - aw) / pl.splits));
   pl.tpart = (size_t)pl.splits * Mm * pl.npad;
   return pl;
@@ -453,28 +508,20 @@ hipError_t launch_gemv(const uint16_t* X, int64_t M, int64_t K, int64_t N, const
   const uint64_t nchunk = (uint64_t)N * K / 64, nblk = ((uint64_t)N * K) >> w.bshift;
   GemvParams p{X, M, K, N, w, nchunk * kBlockBytes, w.dq ? nblk : nblk * 4, w.dq ? ((nblk + 255) / 256) * 4 : 0,
                A, r, partial, partial + pl.tpart, pl.npad, pl.agroups * GROWS, pl.splits, pl.rgroups,
-               pl.rranges, pl.agroups, pl.asplits, nf4_table(w.cb)};
-  const size_t lds = std::max(kLdsWeight, kLdsAdapter);
+               pl.rranges, pl.agroups, pl.asplits, pl.ngr, nf4_table(w.cb)};
+  const size_t lds = std::max(kLdsWeight * pl.tg, kLdsAdapter);
   ProfScope ps("k_fwd_nf4_gemv", s);
-  const dim3 grid((unsigned)(pl.rranges * pl.splits + pl.agroups * pl.asplits));
+  const dim3 grid((unsigned)(pl.rranges * pl.splits + pl.agroups * pl.asplits * pl.ngr));
   const int bm = w.bshift == 6 ? 0 : w.bshift > 6 ? 1 : 2;
-  const dim3 block(GT);
-  if (w.dq) {
-    if (bm == 0) hipLaunchKernelGGL((k_fwd_nf4_gemv<true, 0>), grid, block, lds, s, p);
-    else if (bm == 1) hipLaunchKernelGGL((k_fwd_nf4_gemv<true, 1>), grid, block, lds, s, p);
-    else hipLaunchKernelGGL((k_fwd_nf4_gemv<true, 2>), grid, block, lds, s, p);
-  } else {
-    if (bm == 0) hipLaunchKernelGGL((k_fwd_nf4_gemv<false, 0>), grid, block, lds, s, p);
-    else if (bm == 1) hipLaunchKernelGGL((k_fwd_nf4_gemv<false, 1>), grid, block, lds, s, p);
-    else hipLaunchKernelGGL((k_fwd_nf4_gemv<false, 2>), grid, block, lds, s, p);
-  }
+  launch_gemv_variant<1>(w.dq != 0, bm, pl.tg, grid, lds, p, s);
   return hipGetLastError();
 }
 
 hipError_t launch_gemv_epilogue(const float* partial, const GemvPlan& pl, int64_t M, int64_t N, const uint16_t* B,
                                 int64_t r, float scale, uint16_t* Y, uint16_t* T_save, hipStream_t s) {
   ProfScope ps("k_gemv_epilogue", s);
-  hipLaunchKernelGGL(k_gemv_epilogue, dim3((unsigned)((N + 63) / 64)), dim3(256), 0, s, partial, pl.splits,
+  hipLaunchKernelGGL(k_gemv_epilogue, dim3((unsigned)((N + 63) / 64), (unsigned)pl.ngr), dim3(256), 0, s, partial,
+                     pl.splits,
                      partial + pl.tpart, pl.asplits, M, N, pl.npad, pl.agroups * GROWS, B, r, scale, Y, T_save);
   return hipGetLastError();
 }

@@ -80,7 +80,7 @@ hipError_t launch_fwd_gemm(const uint16_t* X, int64_t M, int64_t K, int64_t N, c
                            const uint16_t* Ts, int64_t rp, const uint16_t* B, int64_t r, uint16_t* Y,
                            hipStream_t s);
 
-// ---- fused forward, skinny M <= 16 (gemv.hip) ---------------------------------------------
+// ---- fused forward, few tokens M <= 64 (gemv.hip) ---------------------------------------------
 // k_fwd_nf4_gemv writes fp32 partials: partial[split][m][n] (X deq(W)^T over `splits` slices
 // of the reduction) and, at float offset tpart, tpartial[aslice][m][j] (X A over `asplits`
 // slices of ka rows); launch_gemv_epilogue forms T, Ts = bf16(s T), T_save = bf16(T) when
@@ -92,6 +92,8 @@ struct GemvPlan {
   int64_t npad;               // weight partial row length (rgroups * 16)
   int64_t agroups;            // 64-column adapter groups
   int asplits;                // adapter slices of 2048 rows of A
+  int ngr;                    // 16-token groups of the batch (ceil(M / 16))
+  int tg;                     // token groups each weight lane feeds (1, 2 or 4 >= ngr)
   size_t tpart;               // float offset of the adapter partials
 };
 GemvPlan gemv_plan(int64_t M, int64_t K, int64_t N, int64_t rp);

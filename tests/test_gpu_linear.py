@@ -61,7 +61,7 @@ def test_c1_config():
 SMALL = [
     # (M, in, out, r, alpha) -- several tiles and ragged tails of each dimension
     (100, 320, 200, 8, 16.0),      # ragged M, in not a multiple of the 128 dX tile, out not of the 128 fwd tile
-    (17, 256, 264, 16, 32.0),      # just above the skinny-M threshold
+    (17, 256, 264, 16, 32.0),      # two 16-token groups on the skinny path, one of a single token
     (300, 128, 512, 72, 16.0),     # rank padded to 128
     (513, 1024, 1024, 64, 16.0),   # 3 token tiles, 8 feature tiles
     (1, 64, 8, 8, 16.0),           # smallest legal layer
@@ -99,6 +99,31 @@ def test_many_token_rank_products(M, din, dout, r):
     inp = workloads.custom_linear(M, din, dout, r, seed=M + din + dout + r)
     _check_full(inp, label=f"rank-r{(M, din, dout, r)}")
     _check_full(inp, save_T=False, label=f"rank-r{(M, din, dout, r)} recompute-T")
+
+
+SKINNY_GROUPS = [
+    # (M, in, out, r): batches of 17..64 tokens on the weight-streaming path (2 or 4 groups of
+    # 16 tokens per weight lane), with ragged token groups, slices and row groups
+    (32, 2048, 1000, 64),
+    (33, 320, 264, 16),        # three token groups, the third of one token (run as four)
+    (48, 4096, 4104, 256),
+    (64, 1024, 1536, 64),
+    (64, 2304, 264, 24),
+    (65, 512, 384, 16),        # just above: the large-M path
+]
+
+
+@pytest.mark.parametrize("M,din,dout,r", SKINNY_GROUPS)
+def test_skinny_token_groups(M, din, dout, r):
+    inp = workloads.custom_linear(M, din, dout, r, seed=M * 3 + din + r)
+    _check_full(inp, backward=False, label=f"skinny{(M, din, dout, r)}")
+    _check_full(inp, backward=False, save_T=False, label=f"skinny{(M, din, dout, r)} no-T")
+
+
+@pytest.mark.parametrize("dq,block", [(False, 64), (True, 32), (True, 256)])
+def test_skinny_token_groups_formats(dq, block):
+    inp = workloads.custom_linear(40, 1024, 520, 8, seed=41 + block)
+    _check_full(inp, dq=dq, block=block, backward=False, label=f"skinny40 dq={dq} block={block}")
 
 
 @pytest.mark.parametrize("dq", [True, False])
@@ -225,7 +250,19 @@ def test_c4_skinny_full(idx):
     """Skinny forward at 65B shapes; every token row checked, on sampled output columns."""
     require_gpu()
     lin = workloads.CONFIGS[4].linears[idx]
-    inp = workloads.linear_inputs(4, lin)
+    _check_skinny_columns(workloads.linear_inputs(4, lin), idx)
+
+
+@pytest.mark.parametrize("which", [0, 1])
+def test_skinny_64_tokens_65b_shapes(which):
+    """64 tokens (four groups of 16) at the 65B shapes, on sampled output columns."""
+    require_gpu()
+    din, dout = ((8192, 22016), (22016, 8192))[which]
+    _check_skinny_columns(workloads.custom_linear(64, din, dout, 64, seed=640 + which, alpha=16.0), 10 + which)
+
+
+def _check_skinny_columns(inp, idx):
+    lin = inp.spec
     log("skinny", lin.name, f"M={lin.M} in={lin.d_in} out={lin.d_out}")
     g = _run(inp, backward=False)
     cols = np.sort(np.random.default_rng(idx).choice(lin.d_out, 96, replace=False))
