@@ -169,6 +169,19 @@ SmallGemm gemm_dB(const uint16_t* T, int64_t ldT, const uint16_t* dY, int64_t M,
 
 bool use_gemv(int64_t M) { return M <= 64; }   // few tokens: the weight-streaming path
 
+// 65..256 tokens fill one 256-token panel of the large-M GEMM, whose out/128 feature tiles
+// then leave most of the GPU idle: cut the reduction into slices of `stages` stages so
+// that tiles x slices come to about one workgroup per CU (at least 4 stages a slice).
+// Returns the stages per slice, or 0 for the plain path.
+int64_t split_stages(int64_t M, int64_t in, int64_t out) {
+  if (M <= 64 || M > 256) return 0;
+  const int64_t tiles = (out + 127) / 128, nkb = in / 64;
+  const int64_t s = std::min((256 + tiles / 2) / tiles, nkb / 4);
+  if (s < 2) return 0;
+  return (nkb + s - 1) / s;
+}
+int64_t split_count(int64_t in, int64_t stages) { return (in / 64 + stages - 1) / stages; }
+
 LoraEpi epi_none() { return LoraEpi{nullptr, 0, 0.0f, nullptr, 0, 0.0f, nullptr, 0.0f}; }
 
 struct FwdWs {
@@ -186,7 +199,12 @@ FwdWs fwd_layout(void* base, int64_t M, int64_t in, int64_t out, int32_t r) {
   FwdWs ws;
   ws.t = lora_problem(gemm_T(nullptr, nullptr, Mm, in, r), epi_none(), kMaxSplits);
   ws.gv = gemv_plan(Mm, in, out, rp);
-  const size_t pf = use_gemv(M) ? gemv_partial_floats(ws.gv, Mm) : lora_partial_floats(ws.t);
+  const int64_t st = split_stages(M, in, out);
+  if (st) {   // the split forward's slices take the place of the weight slices
+    ws.gv.splits = (int)split_count(in, st);
+    ws.gv.tpart = (size_t)ws.gv.splits * Mm * ws.gv.npad;
+  }
+  const size_t pf = use_gemv(M) || st ? gemv_partial_floats(ws.gv, Mm) : lora_partial_floats(ws.t);
   ws.Ts = c.take<uint16_t>((size_t)Mm * rp);
   ws.partial = c.take<float>(std::max<size_t>(pf, 1));
   ws.bytes = round_up(c.off, 256);
@@ -355,6 +373,14 @@ qlora_status qlora_linear_fwd(const uint16_t* X, int64_t M, const qlora_nf4* w, 
     // few tokens: one pass over the packed weight that also forms the partials of X A, then
     // an epilogue that finishes T, Ts and Y
     QL_HIP(launch_gemv(X, M, in, out, v, A, r, L.gv, L.partial, stream));
+    QL_HIP(launch_gemv_epilogue(L.partial, L.gv, M, out, B, r, scale, Y, T_save, stream));
+    return QLORA_OK;
+  }
+  if (const int64_t st = split_stages(M, in, out)) {
+    // one token panel, few feature tiles: X A partials, the GEMM in K-slices (fp32 partials),
+    // and the weight-streaming path's epilogue for the sums, T, Ts B and Y
+    QL_HIP(launch_gemv(X, M, in, out, v, A, r, L.gv, L.partial, stream, true));
+    QL_HIP(launch_fwd_gemm_split(X, M, in, out, v, (int)st, L.partial, L.gv.npad, stream));
     QL_HIP(launch_gemv_epilogue(L.partial, L.gv, M, out, B, r, scale, Y, T_save, stream));
     return QLORA_OK;
   }

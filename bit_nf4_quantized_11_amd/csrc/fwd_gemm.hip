@@ -31,6 +31,10 @@ struct FwdParams {
   int64_t r;
   uint16_t* Y;
   NF4Table tab;
+  // split mode: K-slices of `spl` stages, fp32 partials [split][M][npad], no adapter stages
+  float* partial;
+  int64_t npad;
+  uint32_t spl;
 };
 
 struct WRegs {
@@ -47,21 +51,28 @@ struct Stage {
 // BM: 0 for blocks of 64 (one block per row per stage), 1 for 128 and 256 (a block spans
 // 2 or 4 stages), 2 for 32 (two blocks per row per stage: the two halves of a quad use
 // different scales, so each lane builds the whole 16-entry table itself).
-template <bool DQ, int BM>
+// SPLIT: a workgroup covers stages [spl s, spl (s + 1)) of its tile's reduction and writes
+// fp32 partial sums (few tokens: the K-slices give the GPU enough workgroups); the adapter
+// term and the final sum come from the weight-streaming path's epilogue.
+template <bool DQ, int BM, bool SPLIT>
 __global__ __launch_bounds__(NT) void k_fwd_nf4_gemm(FwdParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM_ELEMS];
   uint16_t* const sT[2] = {smem, smem + TILE_T};
   uint16_t* const sF[2] = {smem + 2 * TILE_T, smem + 2 * TILE_T + TILE_F};
 
   int64_t tt, tf;
-  tile_of((p.M + BT - 1) / BT, (p.N + BF - 1) / BF, tt, tf);
+  const int64_t tiles_t = (p.M + BT - 1) / BT, tiles_f = (p.N + BF - 1) / BF;
+  const uint32_t split = SPLIT ? (uint32_t)(blockIdx.x / (tiles_t * tiles_f)) : 0u;
+  tile_of(tiles_t, tiles_f, tt, tf, SPLIT ? (int64_t)blockIdx.x - (int64_t)split * tiles_t * tiles_f : -1);
   const uint32_t m0 = (uint32_t)(tt * BT), n0 = (uint32_t)(tf * BF);
-  const uint32_t nkb = (uint32_t)(p.K / 64);
+  const uint32_t nkb_all = (uint32_t)(p.K / 64);
+  const uint32_t it0 = SPLIT ? split * p.spl : 0u;                       // first stage
+  const uint32_t nkb = SPLIT ? min(nkb_all, it0 + p.spl) - it0 : nkb_all;   // stages of this workgroup
   const int t = threadIdx.x;
   // weight row t/4 of the tile, quarter t%4 of its block (groups 2q and 2q+1 -> chunks
   // 2q, 2q+1 of the LDS row); rows past N read as zero (their outputs are not stored)
   const int wrow = t >> 2, wq = t & 3;
-  const uint32_t wblk0 = (n0 + wrow) * nkb;
+  const uint32_t wblk0 = (n0 + wrow) * nkb_all;
   const uint32_t code_off = wblk0 * kBlockBytes + wq * 8;
 
   const TokenSrc xs = token_src(p.X, (uint64_t)p.M * p.K * 2, (uint32_t)p.K, m0);
@@ -146,25 +157,31 @@ __global__ __launch_bounds__(NT) void k_fwd_nf4_gemm(FwdParams p) {
   // Prefetch loads are unconditional (a stage index past the end is clamped to the last
   // stage and the data is never stored): a load under a branch would make the compiler
   // wait for every load in flight where the branch rejoins.
-  const uint32_t last = nkb - 1;
-  load(0, S0);
-  load(min(1u, last), S1);
+  const uint32_t last = it0 + nkb - 1;
+  load(it0, S0);
+  load(min(it0 + 1, last), S1);
   store_all(S0, 0);
   __syncthreads();
   // two stages per trip (stage it in buffer 0 with it+1 in S1, then it+1 in buffer 1 with
   // it+2 in S0); a single exit keeps the accumulators in one register set
   uint32_t it = 0;
   for (; it + 1 < nkb; it += 2) {
-    load(min(it + 2, last), S0);
+    load(min(it0 + it + 2, last), S0);
     compute_store(acc, 0, S1, 1);
     __syncthreads();
-    load(min(it + 3, last), S1);
+    load(min(it0 + it + 3, last), S1);
     compute_store(acc, 1, S0, 0);
     __syncthreads();
   }
   if (it < nkb) {   // odd number of stages: the last one is in buffer 0
     mma_stage<false>(acc, sT[0], sF[0]);
     __syncthreads();
+  }
+
+  if constexpr (SPLIT) {
+    if (combine_halves(acc, smem))
+      store_out_f32(acc, p.partial + (int64_t)split * p.M * p.npad, p.npad, m0, p.M, n0, p.N);
+    return;
   }
 
   // adapter stages: Ts [M][rp] against rows of B, kept as stored ([j][n]) in the natural
@@ -196,19 +213,43 @@ hipError_t launch_fwd_gemm(const uint16_t* X, int64_t M, int64_t K, int64_t N, c
   // 64-element code chunks, and blocks (one constant each; in is a multiple of the block size)
   const uint64_t nchunk = (uint64_t)N * K / 64, nblk = ((uint64_t)N * K) >> w.bshift;
   FwdParams p{X, M, K, N, w, nchunk * kBlockBytes, w.dq ? nblk : nblk * 4, w.dq ? ((nblk + 255) / 256) * 4 : 0,
-              Ts, rp, B, r, Y, nf4_table(w.cb)};
+              Ts, rp, B, r, Y, nf4_table(w.cb), nullptr, 0, 0};
   const int64_t tiles = ((M + BT - 1) / BT) * ((N + BF - 1) / BF);
   const int bm = w.bshift == 6 ? 0 : w.bshift > 6 ? 1 : 2;
   ProfScope ps("k_fwd_nf4_gemm", s);
   const dim3 grid((unsigned)tiles), block(NT);
   if (w.dq) {
-    if (bm == 0) hipLaunchKernelGGL((k_fwd_nf4_gemm<true, 0>), grid, block, 0, s, p);
-    else if (bm == 1) hipLaunchKernelGGL((k_fwd_nf4_gemm<true, 1>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((k_fwd_nf4_gemm<true, 2>), grid, block, 0, s, p);
+    if (bm == 0) hipLaunchKernelGGL((k_fwd_nf4_gemm<true, 0, false>), grid, block, 0, s, p);
+    else if (bm == 1) hipLaunchKernelGGL((k_fwd_nf4_gemm<true, 1, false>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((k_fwd_nf4_gemm<true, 2, false>), grid, block, 0, s, p);
   } else {
-    if (bm == 0) hipLaunchKernelGGL((k_fwd_nf4_gemm<false, 0>), grid, block, 0, s, p);
-    else if (bm == 1) hipLaunchKernelGGL((k_fwd_nf4_gemm<false, 1>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((k_fwd_nf4_gemm<false, 2>), grid, block, 0, s, p);
+    if (bm == 0) hipLaunchKernelGGL((k_fwd_nf4_gemm<false, 0, false>), grid, block, 0, s, p);
+    else if (bm == 1) hipLaunchKernelGGL((k_fwd_nf4_gemm<false, 1, false>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((k_fwd_nf4_gemm<false, 2, false>), grid, block, 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_gemm_split(const uint16_t* X, int64_t M, int64_t K, int64_t N, const NF4View& w, int stages,
+                                 float* partial, int64_t npad, hipStream_t s) {
+  const uint64_t nchunk = (uint64_t)N * K / 64, nblk = ((uint64_t)N * K) >> w.bshift;
+  const uint32_t nkb = (uint32_t)(K / 64);
+  const uint32_t spl = (uint32_t)stages;
+  FwdParams p{X, M, K, N, w, nchunk * kBlockBytes, w.dq ? nblk : nblk * 4, w.dq ? ((nblk + 255) / 256) * 4 : 0,
+              nullptr, 0, nullptr, 0, nullptr, nf4_table(w.cb), partial, npad, spl};
+  const int64_t tiles = ((M + BT - 1) / BT) * ((N + BF - 1) / BF);
+  const int64_t used = (nkb + spl - 1) / spl;   // splits that get at least one stage
+  ProfScope ps("k_fwd_nf4_gemm", s);
+  const dim3 grid((unsigned)(tiles * used)), block(NT);
+  const int bm = w.bshift == 6 ? 0 : w.bshift > 6 ? 1 : 2;
+  if (w.dq) {
+    if (bm == 0) hipLaunchKernelGGL((k_fwd_nf4_gemm<true, 0, true>), grid, block, 0, s, p);
+    else if (bm == 1) hipLaunchKernelGGL((k_fwd_nf4_gemm<true, 1, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((k_fwd_nf4_gemm<true, 2, true>), grid, block, 0, s, p);
+  } else {
+    if (bm == 0) hipLaunchKernelGGL((k_fwd_nf4_gemm<false, 0, true>), grid, block, 0, s, p);
+    else if (bm == 1) hipLaunchKernelGGL((k_fwd_nf4_gemm<false, 1, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((k_fwd_nf4_gemm<false, 2, true>), grid, block, 0, s, p);
   }
   return hipGetLastError();
 }

@@ -303,6 +303,28 @@ __device__ __forceinline__ void store_out(const Acc& a, uint16_t* __restrict__ o
   }
 }
 
+// Store the fp32 accumulators of this wave's quarter into out [ntok][ld] (ld % 4 == 0, 16-byte
+// aligned rows), features below nfeat only.
+__device__ __forceinline__ void store_out_f32(const Acc& a, float* __restrict__ out, int64_t ld, int64_t m0,
+                                              int64_t ntok, int64_t f0, int64_t nfeat) {
+  const int lane = threadIdx.x & 63;
+  const int wt = wave_t(), wf = wave_f();
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int64_t tok = m0 + wt * 128 + m * 32 + (lane & 31);
+    if (tok >= ntok) continue;
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int64_t feat = f0 + wf * 64 + f * 32 + 8 * g + 4 * (lane >> 5);
+        if (feat >= nfeat) continue;
+        const f32x16 v = a.c[f][m];
+        *reinterpret_cast<float4*>(out + tok * ld + feat) = make_float4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
+      }
+  }
+}
+
 // ---- NF4 weight producer --------------------------------------------------------------------
 // Per stage every thread dequantizes 16 weights (8 code bytes, a quarter of a block); the
 // four threads of a block sit in one DPP quad (lanes 4j..4j+3, quarter = lane % 4) and
@@ -348,9 +370,10 @@ __device__ __forceinline__ Planes quad_planes(const QuadLevels& L, float s) {
 // Map a linear workgroup id to a (token tile, feature tile) pair.  Workgroups are
 // dispatched round-robin over the 8 XCDs; give each XCD a contiguous run of tiles
 // (token-tile major) so the tiles sharing a token panel share an L2.
-__device__ __forceinline__ void tile_of(int64_t tiles_t, int64_t tiles_f, int64_t& tt, int64_t& tf) {
+__device__ __forceinline__ void tile_of(int64_t tiles_t, int64_t tiles_f, int64_t& tt, int64_t& tf,
+                                        int64_t id = -1) {
   const int64_t n = tiles_t * tiles_f;
-  int64_t L = blockIdx.x;
+  int64_t L = id < 0 ? (int64_t)blockIdx.x : id;
   if ((n & 7) == 0) L = (L & 7) * (n >> 3) + (L >> 3);
   tt = L / tiles_f;
   tf = L - tt * tiles_f;

@@ -503,7 +503,7 @@ size_t gemv_partial_floats(const GemvPlan& pl, int64_t M) {
 }
 
 hipError_t launch_gemv(const uint16_t* X, int64_t M, int64_t K, int64_t N, const NF4View& w, const uint16_t* A,
-                       int64_t r, const GemvPlan& pl, float* partial, hipStream_t s) {
+                       int64_t r, const GemvPlan& pl, float* partial, hipStream_t s, bool adapters_only) {
   // 64-element code chunks, and blocks (one constant each; in is a multiple of the block size)
   const uint64_t nchunk = (uint64_t)N * K / 64, nblk = ((uint64_t)N * K) >> w.bshift;
   GemvParams p{X, M, K, N, w, nchunk * kBlockBytes, w.dq ? nblk : nblk * 4, w.dq ? ((nblk + 255) / 256) * 4 : 0,
@@ -511,7 +511,8 @@ hipError_t launch_gemv(const uint16_t* X, int64_t M, int64_t K, int64_t N, const
                pl.rranges, pl.agroups, pl.asplits, pl.ngr, nf4_table(w.cb)};
   const size_t lds = std::max(kLdsWeight * pl.tg, kLdsAdapter);
   ProfScope ps("k_fwd_nf4_gemv", s);
-  const dim3 grid((unsigned)(pl.rranges * pl.splits + pl.agroups * pl.asplits * pl.ngr));
+  const int64_t n_adapter = pl.agroups * pl.asplits * pl.ngr;
+  const dim3 grid((unsigned)((adapters_only ? 0 : pl.rranges * pl.splits) + n_adapter));
   const int bm = w.bshift == 6 ? 0 : w.bshift > 6 ? 1 : 2;
   launch_gemv_variant<1>(w.dq != 0, bm, pl.tg, grid, lds, p, s);
   return hipGetLastError();

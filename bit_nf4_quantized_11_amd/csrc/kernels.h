@@ -79,6 +79,11 @@ hipError_t launch_lora_reduce(const LoraProblem& p0, const LoraProblem* p1, cons
 hipError_t launch_fwd_gemm(const uint16_t* X, int64_t M, int64_t K, int64_t N, const NF4View& w,
                            const uint16_t* Ts, int64_t rp, const uint16_t* B, int64_t r, uint16_t* Y,
                            hipStream_t s);
+// Few tokens (one 256-token panel), few feature tiles: the same GEMM cut into K-slices of
+// `stages` 64-deep stages, fp32 partials partial[slice][m][n] (row length npad), no adapter
+// term; ceil(K / 64 / stages) slices.  The epilogue of the weight-streaming path finishes Y.
+hipError_t launch_fwd_gemm_split(const uint16_t* X, int64_t M, int64_t K, int64_t N, const NF4View& w, int stages,
+                                 float* partial, int64_t npad, hipStream_t s);
 
 // ---- fused forward, few tokens M <= 64 (gemv.hip) ---------------------------------------------
 // k_fwd_nf4_gemv writes fp32 partials: partial[split][m][n] (X deq(W)^T over `splits` slices
@@ -98,8 +103,10 @@ struct GemvPlan {
 };
 GemvPlan gemv_plan(int64_t M, int64_t K, int64_t N, int64_t rp);
 size_t gemv_partial_floats(const GemvPlan& pl, int64_t M);
+// adapters_only: launch only the X A workgroups (their partials feed the epilogue after the
+// split large-M forward)
 hipError_t launch_gemv(const uint16_t* X, int64_t M, int64_t K, int64_t N, const NF4View& w, const uint16_t* A,
-                       int64_t r, const GemvPlan& pl, float* partial, hipStream_t s);
+                       int64_t r, const GemvPlan& pl, float* partial, hipStream_t s, bool adapters_only = false);
 hipError_t launch_gemv_epilogue(const float* partial, const GemvPlan& pl, int64_t M, int64_t N, const uint16_t* B,
                                 int64_t r, float scale, uint16_t* Y, uint16_t* T_save, hipStream_t s);
 

@@ -120,6 +120,32 @@ def test_skinny_token_groups(M, din, dout, r):
     _check_full(inp, backward=False, save_T=False, label=f"skinny{(M, din, dout, r)} no-T")
 
 
+SPLIT_FWD = [
+    # (M, in, out, r): 65..256 tokens with few feature tiles: the large-M forward in K-slices
+    # (fp32 partials) finished by the weight-streaming path's epilogue
+    (65, 4096, 4096, 64),      # 8 slices of 8 stages
+    (80, 1344, 392, 16),       # 21 stages in slices of 5 (the last of 1), ragged out
+    (100, 1024, 520, 8),
+    (128, 2048, 1000, 16),
+    (200, 512, 264, 24),       # 2 slices of 4 stages, 13 token groups (the last of 8)
+    (256, 4096, 1024, 256),    # 16 slices, largest rank
+    (257, 1024, 1024, 64),     # two token panels: the plain path
+]
+
+
+@pytest.mark.parametrize("M,din,dout,r", SPLIT_FWD)
+def test_split_forward(M, din, dout, r):
+    inp = workloads.custom_linear(M, din, dout, r, seed=M + din + dout)
+    _check_full(inp, label=f"split{(M, din, dout, r)}")
+    _check_full(inp, save_T=False, backward=False, label=f"split{(M, din, dout, r)} no-T")
+
+
+@pytest.mark.parametrize("dq,block", [(False, 64), (True, 128), (True, 32)])
+def test_split_forward_formats(dq, block):
+    inp = workloads.custom_linear(96, 1024, 520, 8, seed=97 + block)
+    _check_full(inp, dq=dq, block=block, backward=False, label=f"split96 dq={dq} block={block}")
+
+
 @pytest.mark.parametrize("dq,block", [(False, 64), (True, 32), (True, 256)])
 def test_skinny_token_groups_formats(dq, block):
     inp = workloads.custom_linear(40, 1024, 520, 8, seed=41 + block)
