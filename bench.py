@@ -249,6 +249,7 @@ def main():
 
     if args.only in ("all", "gemv") and not args.no_gemv:
         result["gemv"] = bench_gemv(Q, workloads, torch, dev, args.gemv_iters)
+        result["few_tokens"] = bench_few_tokens(Q, workloads, torch, dev)
 
     if args.only in ("all", "headline"):
         result["formats"] = bench_formats(Q, workloads, torch, dev)
@@ -324,6 +325,57 @@ def bench_gemv(Q, workloads, torch, dev, iters):
     out["weight_GBps_min"] = worst
     out["weight_GBps_max"] = best
     out["frac_min"] = worst / PEAK_HBM_GBPS
+    return out
+
+
+def bench_few_tokens(Q, workloads, torch, dev, iters=20):
+    """Forward and backward of the 4096->4096, rank-64 layer for 1..256 tokens, where one
+    256-token panel of the large-M GEMMs would leave most compute units idle: the
+    weight-streaming forward (M <= 64), the forward GEMM in K-slices (65..256 tokens) and
+    the dX GEMM in slices of the weight's rows (M <= 256).  The 8.65 MB packed weight stays
+    in the caches between calls; per-kernel times from the library's own HIP events."""
+    din = dout = 4096
+    r = 64
+    s = 16.0 / r
+    W = workloads.device_normal_bf16(5000, (dout, din), 0.02)
+    w = Q.qlora_quantize_nf4(W, True)
+    del W
+    A = workloads.device_normal_bf16(5001, (din, r), 0.02)
+    B = workloads.device_normal_bf16(5002, (r, dout), 0.02)
+    out = {"shape": "4096->4096, r = 64, NF4 + double quant", "cases": {}}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for M in (1, 16, 64, 128, 256):
+        X = workloads.device_normal_bf16(5003 + M, (M, din), 1.0)
+        dY = workloads.device_normal_bf16(5004 + M, (M, dout), 1.0)
+        ws = torch.empty(max(Q.qlora_fwd_workspace(M, din, dout, r), Q.qlora_bwd_workspace(M, din, dout, r)),
+                         dtype=torch.uint8, device=dev)
+        Y = torch.empty((M, dout), dtype=torch.bfloat16, device=dev)
+        T = torch.empty((M, r), dtype=torch.bfloat16, device=dev)
+        dX = torch.empty((M, din), dtype=torch.bfloat16, device=dev)
+        dA = torch.empty((din, r), dtype=torch.float32, device=dev)
+        dB = torch.empty((r, dout), dtype=torch.float32, device=dev)
+        calls = {"fwd": lambda: Q.qlora_linear_fwd(X, w, A, B, s, Y=Y, T_save=T, workspace=ws),
+                 "bwd": lambda: Q.qlora_linear_bwd(dY, X, T, w, A, B, s, dX=dX, dA=dA, dB=dB, workspace=ws)}
+        case = {}
+        for name, fn in calls.items():
+            for _ in range(5):
+                fn()
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(iters):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            case[f"{name}_us"] = 1e3 * e0.elapsed_time(e1) / iters
+            Q.qlora_profile_enable(True)
+            Q.qlora_profile_read(reset=True)
+            for _ in range(iters):
+                fn()
+            torch.cuda.synchronize()
+            prof = Q.qlora_profile_read(reset=True)
+            Q.qlora_profile_enable(False)
+            case[f"{name}_kernels_us"] = {k: 1e3 * t / n for k, (n, t) in prof.items()}
+        out["cases"][f"M={M}"] = case
     return out
 
 

@@ -182,6 +182,17 @@ int64_t split_stages(int64_t M, int64_t in, int64_t out) {
 }
 int64_t split_count(int64_t in, int64_t stages) { return (in / 64 + stages - 1) / stages; }
 
+// The same for dX with up to 256 tokens (the backward has no weight-streaming path): in/128
+// column tiles, ceil(out/64) reduction stages over the weight's rows.
+int64_t dx_split_stages(int64_t M, int64_t in, int64_t out) {
+  if (M > 256) return 0;
+  const int64_t tiles = (in + 127) / 128, nred = (out + 63) / 64;
+  const int64_t s = std::min((256 + tiles / 2) / tiles, nred / 4);
+  if (s < 2) return 0;
+  return (nred + s - 1) / s;
+}
+int64_t dx_split_count(int64_t out, int64_t stages) { return ((out + 63) / 64 + stages - 1) / stages; }
+
 LoraEpi epi_none() { return LoraEpi{nullptr, 0, 0.0f, nullptr, 0, 0.0f, nullptr, 0.0f}; }
 
 struct FwdWs {
@@ -228,8 +239,10 @@ BwdWs bwd_layout(void* base, int64_t M, int64_t in, int64_t out, int32_t r) {
   ws.g = lora_problem(gemm_G(nullptr, nullptr, Mm, out, r), epi_none(), kMaxSplits);
   ws.da = lora_problem(gemm_dA(nullptr, nullptr, Mm, in, r, rp), epi_none(), kMaxSplits);
   ws.db = lora_problem(gemm_dB(nullptr, r, nullptr, Mm, out, r), epi_none(), kMaxSplits);
+  const int64_t dst = dx_split_stages(M, in, out);
+  const size_t pdx = dst ? (size_t)dx_split_count(out, dst) * Mm * in : 0;   // split dX partials
   const size_t pf = std::max({lora_partial_floats(ws.t), lora_partial_floats(ws.g),
-                              lora_partial_floats(ws.da) + lora_partial_floats(ws.db)});
+                              lora_partial_floats(ws.da) + lora_partial_floats(ws.db), pdx});
   ws.Gs = c.take<uint16_t>((size_t)Mm * rp);
   ws.T = c.take<uint16_t>((size_t)Mm * r);
   ws.partial = c.take<float>(std::max<size_t>(pf, 1));
@@ -430,7 +443,16 @@ qlora_status qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, const uint1
   pg.partial = L.partial;
   QL_HIP(launch_lora(pg, nullptr, "k_lora_dyb", stream));
   if (pg.splits > 1) QL_HIP(launch_lora_reduce(pg, nullptr, "k_lora_dyb_reduce", stream));
-  if (dX) QL_HIP(launch_dx_gemm(dY, M, in, out, v, L.Gs, rp, A, r, dX, stream));
+  if (dX) {
+    if (const int64_t dst = dx_split_stages(M, in, out)) {
+      // few tokens, few column tiles: the reduction in slices (fp32 partials), then the
+      // slices' sum plus Gs A^T in one epilogue; the partials of Gs are consumed by now
+      QL_HIP(launch_dx_gemm_split(dY, M, in, out, v, (int)dst, L.partial, stream));
+      QL_HIP(launch_dx_split_epilogue(L.partial, (int)dx_split_count(out, dst), M, in, L.Gs, rp, A, r, dX, stream));
+    } else {
+      QL_HIP(launch_dx_gemm(dY, M, in, out, v, L.Gs, rp, A, r, dX, stream));
+    }
+  }
   // dA = X^T Gs and dB = s T^T dY, one launch for both products and one for both reductions
   LoraProblem pa = lora_problem(gemm_dA(X, L.Gs, M, in, r, rp),
                                 LoraEpi{nullptr, 0, 0.0f, nullptr, 0, 0.0f, dA, 1.0f}, kMaxSplits);

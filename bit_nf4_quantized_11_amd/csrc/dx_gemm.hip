@@ -9,6 +9,10 @@
 // rows x 128 columns) is dequantized into the natural LDS tile as stored and the
 // MFMA operand is gathered with transposing LDS reads.  The adapter stages use the
 // feature-major tile: A is [K][r].
+//
+// Split mode (few tokens, few column tiles): a workgroup covers a slice of the reduction
+// stages, skips the adapter stages and writes fp32 partials; k_dx_split_epilogue sums the
+// slices in order, adds Gs A~^T and rounds once.
 #include "common.h"
 #include "gemm_core.h"
 #include "kernels.h"
@@ -30,6 +34,9 @@ struct DxParams {
   int64_t r;
   uint16_t* dX;
   NF4Table tab;
+  // split mode: slices of `spl` stages, fp32 partials [split][M][K], no adapter stages
+  float* partial;
+  uint32_t spl;
 };
 
 struct WRegs {
@@ -46,18 +53,22 @@ struct Stage {
 // RAGGED: N % 64 != 0, the last stage's token columns past N are masked to zero.
 // BM: 0 for blocks of 64, 1 for 128 and 256 (a block spans two or four 64-column
 // halves of a row), 2 for 32 (two blocks per quad: each lane builds its own table).
-template <bool DQ, bool RAGGED, int BM>
+template <bool DQ, bool RAGGED, int BM, bool SPLIT>
 __global__ __launch_bounds__(NT) void k_bwd_dx_nf4_gemm(DxParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM_ELEMS];
   uint16_t* const sT[2] = {smem, smem + TILE_T};
   uint16_t* const sF[2] = {smem + 2 * TILE_T, smem + 2 * TILE_T + TILE_F};
 
+  const int64_t tiles_t = (p.M + BT - 1) / BT, tiles_f = (p.K + BF - 1) / BF;
+  const uint32_t split = SPLIT ? (uint32_t)(blockIdx.x / (tiles_t * tiles_f)) : 0u;
   int64_t tt, tf;
-  tile_of((p.M + BT - 1) / BT, (p.K + BF - 1) / BF, tt, tf);
+  tile_of(tiles_t, tiles_f, tt, tf, SPLIT ? (int64_t)blockIdx.x - (int64_t)split * tiles_t * tiles_f : -1);
   const uint32_t m0 = (uint32_t)(tt * BT), k0 = (uint32_t)(tf * BF);
   const uint32_t nkb = (uint32_t)(p.K / 64);
   const uint32_t N = (uint32_t)p.N;
-  const uint32_t nred = (N + 63) / 64;   // reduction stages over the weight rows
+  const uint32_t nred_all = (N + 63) / 64;   // reduction stages over the weight rows
+  const uint32_t it0 = SPLIT ? split * p.spl : 0u;                            // first stage
+  const uint32_t nred = SPLIT ? min(nred_all, it0 + p.spl) - it0 : nred_all;   // stages of this workgroup
   const int t = threadIdx.x;
   // NF4 stage mapping: weight row t/8 of the stage, block k0/64 + b (b = (t/4)%2), quarter
   // q = t%4 (groups 2q, 2q+1 -> chunks 8b+2q, 8b+2q+1 of the natural row).  Rows past N
@@ -141,25 +152,31 @@ __global__ __launch_bounds__(NT) void k_bwd_dx_nf4_gemm(DxParams p) {
   // Prefetch loads are unconditional (a stage index past the end is clamped to the last
   // stage and the data is never stored): a load under a branch would make the compiler
   // wait for every load in flight where the branch rejoins.
-  const uint32_t last = nred - 1;
-  load(0, S0);
-  load(min(1u, last), S1);
+  const uint32_t last = it0 + nred - 1;
+  load(it0, S0);
+  load(min(it0 + 1, last), S1);
   store_all(S0, 0);
   __syncthreads();
   // two stages per trip (stage it in buffer 0 with it+1 in S1, then it+1 in buffer 1 with
   // it+2 in S0); a single exit keeps the accumulators in one register set
   uint32_t it = 0;
   for (; it + 1 < nred; it += 2) {
-    load(min(it + 2, last), S0);
+    load(min(it0 + it + 2, last), S0);
     compute_store(acc, 0, S1, 1);
     __syncthreads();
-    load(min(it + 3, last), S1);
+    load(min(it0 + it + 3, last), S1);
     compute_store(acc, 1, S0, 0);
     __syncthreads();
   }
   if (it < nred) {   // odd number of stages: the last one is in buffer 0
     mma_stage<true>(acc, sT[0], sF[0]);
     __syncthreads();
+  }
+
+  if constexpr (SPLIT) {
+    if (combine_halves(acc, smem))
+      store_out_f32(acc, p.partial + (int64_t)split * p.M * p.K, p.K, m0, p.M, k0, p.K);
+    return;
   }
 
   // adapter stages: Gs [M][rp] against rows of A (feature-major: A is [K][r]).  Columns
@@ -182,20 +199,125 @@ __global__ __launch_bounds__(NT) void k_bwd_dx_nf4_gemm(DxParams p) {
   if (combine_halves(acc, smem)) store_out(acc, p.dX, p.K, m0, p.M, k0, p.K);
 }
 
-// dispatch over the template flags (DQ, RAGGED, BM)
-template <int BM>
+// dX[m][i] = bf16( sum over slices of partial[slice][m][i] + sum_{j<r} Gs[m][j] A[i][j] ):
+// the split GEMM's slices in order, then the adapter term, rounded once.  A workgroup
+// covers 64 columns i of one 16-token group (blockIdx.y); thread t takes column t % 64 for
+// the tokens t / 64 + 4 q of the group.  Rows i0..i0+63 of A are one contiguous run of
+// 64 r values: loaded coalesced and kept transposed in LDS ([j][64]); the group's rows of
+// Gs are kept as fp32.  All loads are issued before any is used.
+__global__ __launch_bounds__(256) void k_dx_split_epilogue(const float* __restrict__ partial, int splits, int64_t M,
+                                                          int64_t K, const uint16_t* __restrict__ Gs, int64_t rp,
+                                                          const uint16_t* __restrict__ A, int64_t r,
+                                                          uint16_t* __restrict__ dX) {
+  __shared__ __attribute__((aligned(16))) float sG[16 * 256];
+  __shared__ __attribute__((aligned(16))) uint16_t sA[256 * 64];
+  const int t = threadIdx.x;
+  const int c = t & 63, mq = t >> 6;
+  const int64_t i0 = (int64_t)blockIdx.x * 64;   // K is a multiple of 64: every column exists
+  const int64_t m0 = (int64_t)blockIdx.y * 16;
+  const int Mg = (int)min<int64_t>(16, M - m0);
+  const int mcap = Mg - 1;
+  partial += m0 * K + i0 + c;   // row m of the group: partial[(sp M + m) K]
+
+  // weight partials of the first 8 slices (slice indices past the end repeat the last one, unused)
+  float v[8][4];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int sp = min(u, splits - 1);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[u][q] = partial[((int64_t)sp * M + min(mq + 4 * q, mcap)) * K];
+  }
+  // A[i0..i0+63][0..r): 8 r pieces of 16 bytes, at most 8 per thread; pieces past the run
+  // get an offset past the end of A and read zero
+  const rsrc_t rA = make_rsrc(A, (uint64_t)K * r * 2);
+  const int apieces = (int)r * 8;
+  const uint32_t abase = (uint32_t)(i0 * r * 2), aend = (uint32_t)(K * r * 2);
+  uint4 av[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int idx = t + 256 * u;
+    av[u] = ld16(rA, idx < apieces ? abase + (uint32_t)idx * 16 : aend);
+  }
+  // Gs rows of the group: Mg rp values, at most 2 pieces per thread
+  const rsrc_t rG = make_rsrc(Gs, (uint64_t)M * rp * 2);
+  const int gpieces = Mg * (int)rp / 8;
+  const uint32_t gbase = (uint32_t)(m0 * rp * 2), gend = (uint32_t)(M * rp * 2);
+  uint4 gv[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int idx = t + 256 * u;
+    gv[u] = ld16(rG, idx < gpieces ? gbase + (uint32_t)idx * 16 : gend);
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int idx = t + 256 * u;
+    if (idx < apieces) {
+      const int e = idx * 8, il = e / (int)r, j = e - il * (int)r;   // r % 8 == 0: a piece stays in its row
+      const uint32_t w[4] = {av[u].x, av[u].y, av[u].z, av[u].w};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) sA[(j + k) * 64 + il] = (uint16_t)(w[k >> 1] >> (16 * (k & 1)));
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int idx = t + 256 * u;
+    if (idx < gpieces) {
+      const int e = idx * 8, m = e / (int)rp, j = e - m * (int)rp;
+      const uint32_t w[4] = {gv[u].x, gv[u].y, gv[u].z, gv[u].w};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) sG[m * 256 + j + k] = bf16_to_f32((uint16_t)(w[k >> 1] >> (16 * (k & 1))));
+    }
+  }
+  __syncthreads();
+  float acc[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    acc[q] = v[0][q];
+#pragma unroll
+    for (int u = 1; u < 8; ++u)
+      if (u < splits) acc[q] = __fadd_rn(acc[q], v[u][q]);
+  }
+  for (int sp = 8; sp < splits; ++sp) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] = __fadd_rn(acc[q], partial[((int64_t)sp * M + min(mq + 4 * q, mcap)) * K]);
+  }
+  // Gs A~^T from LDS, four adapter columns at a time (r is a multiple of 8).  Rows of sG
+  // past the group are never written; their sums are not stored.
+  float lora[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int jj = 0; jj < (int)r; jj += 4) {
+    float a[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = bf16_to_f32(sA[(jj + i) * 64 + c]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 g = *reinterpret_cast<const float4*>(sG + (mq + 4 * q) * 256 + jj);
+      lora[q] = __builtin_fmaf(g.x, a[0], lora[q]);
+      lora[q] = __builtin_fmaf(g.y, a[1], lora[q]);
+      lora[q] = __builtin_fmaf(g.z, a[2], lora[q]);
+      lora[q] = __builtin_fmaf(g.w, a[3], lora[q]);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int m = mq + 4 * q;
+    if (m < Mg) dX[(m0 + m) * K + i0 + c] = (uint16_t)f32_to_bf16_bits(__fadd_rn(acc[q], lora[q]));
+  }
+}
+
+// dispatch over the template flags (DQ, RAGGED, BM, SPLIT)
+template <int BM, bool SPLIT>
 void launch_dx_variant(bool dq, bool ragged, int bm, dim3 grid, dim3 block, const DxParams& p, hipStream_t s) {
   if constexpr (BM < 2) {
-    if (bm != BM) return launch_dx_variant<BM + 1>(dq, ragged, bm, grid, block, p, s);
+    if (bm != BM) return launch_dx_variant<BM + 1, SPLIT>(dq, ragged, bm, grid, block, p, s);
   }
   if (dq && !ragged)
-    hipLaunchKernelGGL((k_bwd_dx_nf4_gemm<true, false, BM>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((k_bwd_dx_nf4_gemm<true, false, BM, SPLIT>), grid, block, 0, s, p);
   else if (dq)
-    hipLaunchKernelGGL((k_bwd_dx_nf4_gemm<true, true, BM>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((k_bwd_dx_nf4_gemm<true, true, BM, SPLIT>), grid, block, 0, s, p);
   else if (!ragged)
-    hipLaunchKernelGGL((k_bwd_dx_nf4_gemm<false, false, BM>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((k_bwd_dx_nf4_gemm<false, false, BM, SPLIT>), grid, block, 0, s, p);
   else
-    hipLaunchKernelGGL((k_bwd_dx_nf4_gemm<false, true, BM>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((k_bwd_dx_nf4_gemm<false, true, BM, SPLIT>), grid, block, 0, s, p);
 }
 
 }  // namespace
@@ -206,13 +328,38 @@ hipError_t launch_dx_gemm(const uint16_t* dY, int64_t M, int64_t K, int64_t N, c
   // 64-element code chunks, and blocks (one constant each; in is a multiple of the block size)
   const uint64_t nchunk = (uint64_t)N * K / 64, nblk = ((uint64_t)N * K) >> w.bshift;
   DxParams p{dY, M, K, N, w, nchunk * kBlockBytes, w.dq ? nblk : nblk * 4, w.dq ? ((nblk + 255) / 256) * 4 : 0,
-             Gs, rp, A, r, dX, nf4_table(w.cb)};
+             Gs, rp, A, r, dX, nf4_table(w.cb), nullptr, 0};
   const int64_t tiles = ((M + BT - 1) / BT) * ((K + BF - 1) / BF);
   ProfScope ps("k_bwd_dx_nf4_gemm", s);
   const dim3 grid((unsigned)tiles), block(NT);
   const bool ragged = (N % 64) != 0;
   const int bm = w.bshift == 6 ? 0 : w.bshift > 6 ? 1 : 2;
-  launch_dx_variant<0>(w.dq != 0, ragged, bm, grid, block, p, s);
+  launch_dx_variant<0, false>(w.dq != 0, ragged, bm, grid, block, p, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_dx_gemm_split(const uint16_t* dY, int64_t M, int64_t K, int64_t N, const NF4View& w, int stages,
+                                float* partial, hipStream_t s) {
+  const uint64_t nchunk = (uint64_t)N * K / 64, nblk = ((uint64_t)N * K) >> w.bshift;
+  const uint32_t spl = (uint32_t)stages;
+  DxParams p{dY, M, K, N, w, nchunk * kBlockBytes, w.dq ? nblk : nblk * 4, w.dq ? ((nblk + 255) / 256) * 4 : 0,
+             nullptr, 0, nullptr, 0, nullptr, nf4_table(w.cb), partial, spl};
+  const int64_t tiles = ((M + BT - 1) / BT) * ((K + BF - 1) / BF);
+  const int64_t nred = (N + 63) / 64;
+  const int64_t used = (nred + spl - 1) / spl;   // slices, each with at least one stage
+  ProfScope ps("k_bwd_dx_nf4_gemm", s);
+  const dim3 grid((unsigned)(tiles * used)), block(NT);
+  const bool ragged = (N % 64) != 0;
+  const int bm = w.bshift == 6 ? 0 : w.bshift > 6 ? 1 : 2;
+  launch_dx_variant<0, true>(w.dq != 0, ragged, bm, grid, block, p, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_dx_split_epilogue(const float* partial, int splits, int64_t M, int64_t K, const uint16_t* Gs,
+                                    int64_t rp, const uint16_t* A, int64_t r, uint16_t* dX, hipStream_t s) {
+  ProfScope ps("k_dx_split_epilogue", s);
+  const dim3 grid((unsigned)(K / 64), (unsigned)((M + 15) / 16)), block(256);
+  hipLaunchKernelGGL(k_dx_split_epilogue, grid, block, 0, s, partial, splits, M, K, Gs, rp, A, r, dX);
   return hipGetLastError();
 }
 

@@ -115,6 +115,12 @@ hipError_t launch_gemv_epilogue(const float* partial, const GemvPlan& pl, int64_
 hipError_t launch_dx_gemm(const uint16_t* dY, int64_t M, int64_t K, int64_t N, const NF4View& w,
                           const uint16_t* Gs, int64_t rp, const uint16_t* A, int64_t r, uint16_t* dX,
                           hipStream_t s);
+// few tokens: the reduction in slices of `stages` stages, fp32 partials [slice][M][K]
+// (no adapter term), then the epilogue sums the slices in order, adds Gs A^T, rounds once
+hipError_t launch_dx_gemm_split(const uint16_t* dY, int64_t M, int64_t K, int64_t N, const NF4View& w, int stages,
+                                float* partial, hipStream_t s);
+hipError_t launch_dx_split_epilogue(const float* partial, int splits, int64_t M, int64_t K, const uint16_t* Gs,
+                                    int64_t rp, const uint16_t* A, int64_t r, uint16_t* dX, hipStream_t s);
 
 // ---- adapter merge (merge.hip): out [N][K] = bf16(deq(W) + scale (A B)^T), K % 64 == 0 -------
 hipError_t launch_merge_adapter(const NF4View& w, int64_t N, int64_t K, const uint16_t* A, const uint16_t* B, int64_t r,

@@ -140,6 +140,32 @@ def test_split_forward(M, din, dout, r):
     _check_full(inp, save_T=False, backward=False, label=f"split{(M, din, dout, r)} no-T")
 
 
+SPLIT_DX = [
+    # (M, in, out, r): up to 256 tokens with few dX column tiles: the dX GEMM in slices of
+    # the weight's rows (fp32 partials), then slice sums + Gs A^T in one epilogue
+    (1, 512, 1000, 8),         # 4 slices of 4 stages, ragged last stage (1000 = 15 x 64 + 40)
+    (16, 1024, 4096, 16),      # 16 slices of 4 stages
+    (65, 4096, 4096, 64),      # 8 slices of 8 stages
+    (100, 2048, 520, 8),       # 2 slices (5 + 4 stages), ragged
+    (200, 512, 2056, 24),      # 7 slices of 5 stages (the last of 3), 13 token groups
+    (256, 1024, 4096, 256),    # 16 slices, largest rank
+    (257, 1024, 4096, 64),     # two token panels: the plain path
+]
+
+
+@pytest.mark.parametrize("M,din,dout,r", SPLIT_DX)
+def test_split_backward(M, din, dout, r):
+    inp = workloads.custom_linear(M, din, dout, r, seed=3 * M + din + dout)
+    _check_full(inp, label=f"splitdx{(M, din, dout, r)}")
+    _check_full(inp, save_T=False, label=f"splitdx{(M, din, dout, r)} recompute T")
+
+
+@pytest.mark.parametrize("dq,block", [(False, 64), (True, 128), (True, 32)])
+def test_split_backward_formats(dq, block):
+    inp = workloads.custom_linear(48, 512, 1000, 16, seed=49 + block)
+    _check_full(inp, dq=dq, block=block, label=f"splitdx48 dq={dq} block={block}")
+
+
 @pytest.mark.parametrize("dq,block", [(False, 64), (True, 128), (True, 32)])
 def test_split_forward_formats(dq, block):
     inp = workloads.custom_linear(96, 1024, 520, 8, seed=97 + block)
