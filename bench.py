@@ -102,7 +102,7 @@ def parse():
     ap.add_argument("--gemv-iters", type=int, default=50)
     ap.add_argument("--no-layers", action="store_true", help="skip the 7B MLP pair and the 65B layer stack")
     ap.add_argument("--layer-steps", type=int, default=3, help="timed steps of the 7B MLP pair and the 65B stack")
-    ap.add_argument("--only", choices=["all", "headline", "gemv", "layers", "adamw", "copy"], default="all",
+    ap.add_argument("--only", choices=["all", "headline", "gemv", "few", "layers", "adamw", "copy"], default="all",
                     help="restrict the run (for profiling single kernels); 'copy' runs a plain device copy of "
                          "known size, the reference for scaling hardware byte counters")
     return ap.parse_args()
@@ -249,6 +249,7 @@ def main():
 
     if args.only in ("all", "gemv") and not args.no_gemv:
         result["gemv"] = bench_gemv(Q, workloads, torch, dev, args.gemv_iters)
+    if args.only in ("all", "few"):
         result["few_tokens"] = bench_few_tokens(Q, workloads, torch, dev)
 
     if args.only in ("all", "headline"):
