@@ -330,10 +330,10 @@ def bench_gemv(Q, workloads, torch, dev, iters):
 
 
 def bench_few_tokens(Q, workloads, torch, dev, iters=20):
-    """Forward and backward of the 4096->4096, rank-64 layer for 1..256 tokens, where one
-    256-token panel of the large-M GEMMs would leave most compute units idle: the
-    weight-streaming forward (M <= 64), the forward GEMM in K-slices (65..256 tokens) and
-    the dX GEMM in slices of the weight's rows (M <= 256).  The 8.65 MB packed weight stays
+    """Forward and backward of the 4096->4096, rank-64 layer for 1..1024 tokens, where the
+    few 256-token panels of the large-M GEMMs would leave most compute units idle: the
+    weight-streaming forward (M <= 64), the forward GEMM in K-slices (65..1024 tokens) and
+    the dX GEMM in slices of the weight's rows (M <= 1024).  The 8.65 MB packed weight stays
     in the caches between calls; per-kernel times from the library's own HIP events."""
     din = dout = 4096
     r = 64
@@ -345,7 +345,7 @@ def bench_few_tokens(Q, workloads, torch, dev, iters=20):
     B = workloads.device_normal_bf16(5002, (r, dout), 0.02)
     out = {"shape": "4096->4096, r = 64, NF4 + double quant", "cases": {}}
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    for M in (1, 16, 64, 128, 256):
+    for M in (1, 16, 64, 128, 256, 512, 1024):
         X = workloads.device_normal_bf16(5003 + M, (M, din), 1.0)
         dY = workloads.device_normal_bf16(5004 + M, (M, dout), 1.0)
         ws = torch.empty(max(Q.qlora_fwd_workspace(M, din, dout, r), Q.qlora_bwd_workspace(M, din, dout, r)),

@@ -169,26 +169,35 @@ SmallGemm gemm_dB(const uint16_t* T, int64_t ldT, const uint16_t* dY, int64_t M,
 
 bool use_gemv(int64_t M) { return M <= 64; }   // few tokens: the weight-streaming path
 
-// 65..256 tokens fill one 256-token panel of the large-M GEMM, whose out/128 feature tiles
-// then leave most of the GPU idle: cut the reduction into slices of `stages` stages so
+// Up to 1024 tokens the large-M GEMM has ceil(M/256) token panels x out/128 feature tiles,
+// which can leave most of the GPU idle: cut the reduction into slices of `stages` stages so
 // that tiles x slices come to about one workgroup per CU (at least 4 stages a slice).
-// Returns the stages per slice, or 0 for the plain path.
+// Returns the stages per slice, or 0 for the plain path.  Past one token panel the
+// epilogue's share grows with the panels (at 4096 x 4096: 4 slices for 512 tokens save
+// 15-20 %, 2 slices for 1024 tokens lose 10-16 %), so there the slices must multiply the
+// workgroups at least fourfold.  (Past 1024 tokens the X A workgroups of the
+// weight-streaming kernel, one per 16-token group, would re-read A too often; 64 tokens or
+// fewer take the weight-streaming path itself.)
+constexpr int64_t kSplitMaxTokens = 1024;
+int64_t min_slices(int64_t M) { return M > 256 ? 4 : 2; }
 int64_t split_stages(int64_t M, int64_t in, int64_t out) {
-  if (M <= 64 || M > 256) return 0;
-  const int64_t tiles = (out + 127) / 128, nkb = in / 64;
+  if (M <= 64 || M > kSplitMaxTokens) return 0;
+  const int64_t tiles = ((M + 255) / 256) * ((out + 127) / 128), nkb = in / 64;
+  if (tiles < 1) return 0;   // a size query with an empty dimension
   const int64_t s = std::min((256 + tiles / 2) / tiles, nkb / 4);
-  if (s < 2) return 0;
+  if (s < min_slices(M)) return 0;
   return (nkb + s - 1) / s;
 }
 int64_t split_count(int64_t in, int64_t stages) { return (in / 64 + stages - 1) / stages; }
 
-// The same for dX with up to 256 tokens (the backward has no weight-streaming path): in/128
-// column tiles, ceil(out/64) reduction stages over the weight's rows.
+// The same for dX (the backward has no weight-streaming path, so from one token on):
+// in/128 column tiles per token panel, ceil(out/64) reduction stages over the weight's rows.
 int64_t dx_split_stages(int64_t M, int64_t in, int64_t out) {
-  if (M > 256) return 0;
-  const int64_t tiles = (in + 127) / 128, nred = (out + 63) / 64;
+  if (M > kSplitMaxTokens) return 0;
+  const int64_t tiles = ((M + 255) / 256) * ((in + 127) / 128), nred = (out + 63) / 64;
+  if (tiles < 1) return 0;   // M = 0 (or a size query with an empty dimension)
   const int64_t s = std::min((256 + tiles / 2) / tiles, nred / 4);
-  if (s < 2) return 0;
+  if (s < min_slices(M)) return 0;
   return (nred + s - 1) / s;
 }
 int64_t dx_split_count(int64_t out, int64_t stages) { return ((out + 63) / 64 + stages - 1) / stages; }

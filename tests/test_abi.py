@@ -102,6 +102,10 @@ def test_workspace_queries(lib):
         b = lib.qlora_bwd_workspace(M, 4096, 4096, 64)
         assert f > 0 and b > 0 and f % 256 == 0 and b % 256 == 0
     assert lib.qlora_fwd_workspace(16, 4096, 4096, 300) == 0
+    # queries with an empty dimension answer without dividing by a zero tile count
+    for M, din, dout in ((0, 4096, 4096), (128, 4096, 0), (128, 0, 4096), (512, 0, 0), (0, 0, 0)):
+        assert lib.qlora_fwd_workspace(M, din, dout, 64) >= 0
+        assert lib.qlora_bwd_workspace(M, din, dout, 64) >= 0
 
 
 def _desc(rows=256, cols=256, dq=1, codes=0x10000, absmax=0x20000, c1=0x30000, mu=0x40000, cb=0, block=0):

@@ -121,15 +121,19 @@ def test_skinny_token_groups(M, din, dout, r):
 
 
 SPLIT_FWD = [
-    # (M, in, out, r): 65..256 tokens with few feature tiles: the large-M forward in K-slices
-    # (fp32 partials) finished by the weight-streaming path's epilogue
+    # (M, in, out, r): 65..1024 tokens with few token panels x feature tiles: the large-M
+    # forward in K-slices (fp32 partials) finished by the weight-streaming path's epilogue
     (65, 4096, 4096, 64),      # 8 slices of 8 stages
     (80, 1344, 392, 16),       # 21 stages in slices of 5 (the last of 1), ragged out
     (100, 1024, 520, 8),
     (128, 2048, 1000, 16),
     (200, 512, 264, 24),       # 2 slices of 4 stages, 13 token groups (the last of 8)
     (256, 4096, 1024, 256),    # 16 slices, largest rank
-    (257, 1024, 1024, 64),     # two token panels: the plain path
+    (257, 1024, 1024, 64),     # two token panels x 8 tiles: 4 slices of 4 stages
+    (600, 1024, 520, 16),      # 3 ragged panels x 5 ragged tiles: 4 slices of 4 stages
+    (512, 4096, 4096, 64),     # 2 panels x 32 tiles: 4 slices of 16 stages
+    (1024, 4096, 4096, 64),    # 4 panels x 32 tiles: 2 slices would gain too little, the plain path
+    (1100, 1024, 1024, 64),    # past 1024 tokens: the plain path, ragged last panel
 ]
 
 
@@ -141,15 +145,17 @@ def test_split_forward(M, din, dout, r):
 
 
 SPLIT_DX = [
-    # (M, in, out, r): up to 256 tokens with few dX column tiles: the dX GEMM in slices of
-    # the weight's rows (fp32 partials), then slice sums + Gs A^T in one epilogue
+    # (M, in, out, r): up to 1024 tokens with few token panels x dX column tiles: the dX GEMM
+    # in slices of the weight's rows (fp32 partials), then slice sums + Gs A^T in one epilogue
     (1, 512, 1000, 8),         # 4 slices of 4 stages, ragged last stage (1000 = 15 x 64 + 40)
     (16, 1024, 4096, 16),      # 16 slices of 4 stages
     (65, 4096, 4096, 64),      # 8 slices of 8 stages
     (100, 2048, 520, 8),       # 2 slices (5 + 4 stages), ragged
     (200, 512, 2056, 24),      # 7 slices of 5 stages (the last of 3), 13 token groups
     (256, 1024, 4096, 256),    # 16 slices, largest rank
-    (257, 1024, 4096, 64),     # two token panels: the plain path
+    (257, 1024, 4096, 64),     # two token panels x 8 tiles: 16 slices of 4 stages
+    (700, 2048, 1000, 16),     # 3 ragged panels x 16 tiles: 4 slices of 4 stages, ragged last stage
+    (1100, 1024, 4096, 64),    # past 1024 tokens: the plain path
 ]
 
 
