@@ -172,14 +172,15 @@ bool use_gemv(int64_t M) { return M <= 64; }   // few tokens: the weight-streami
 // Up to 1024 tokens the large-M GEMM has ceil(M/256) token panels x out/128 feature tiles,
 // which can leave most of the GPU idle: cut the reduction into slices of `stages` stages so
 // that tiles x slices come to about one workgroup per CU (at least 4 stages a slice).
-// Returns the stages per slice, or 0 for the plain path.  Past one token panel the
-// epilogue's share grows with the panels (at 4096 x 4096: 4 slices for 512 tokens save
-// 15-20 %, 2 slices for 1024 tokens lose 10-16 %), so there the slices must multiply the
-// workgroups at least fourfold.  (Past 1024 tokens the X A workgroups of the
+// Returns the stages per slice, or 0 for the plain path.  The epilogue's cost grows with
+// the output (M x out) and the slices: 2 slices measured at best even and up to 23 %
+// slower (4096 -> 16384 and 16384 -> 4096 at 128 and 256 tokens, 4096 x 4096 at 1024),
+// 4 or more faster by 15-45 %; so the slices must at least triple the workgroups for one
+// token panel and at least quadruple them past it.  (Past 1024 tokens the X A workgroups of the
 // weight-streaming kernel, one per 16-token group, would re-read A too often; 64 tokens or
 // fewer take the weight-streaming path itself.)
 constexpr int64_t kSplitMaxTokens = 1024;
-int64_t min_slices(int64_t M) { return M > 256 ? 4 : 2; }
+int64_t min_slices(int64_t M) { return M > 256 ? 4 : 3; }
 int64_t split_stages(int64_t M, int64_t in, int64_t out) {
   if (M <= 64 || M > kSplitMaxTokens) return 0;
   const int64_t tiles = ((M + 255) / 256) * ((out + 127) / 128), nkb = in / 64;

@@ -127,7 +127,7 @@ SPLIT_FWD = [
     (80, 1344, 392, 16),       # 21 stages in slices of 5 (the last of 1), ragged out
     (100, 1024, 520, 8),
     (128, 2048, 1000, 16),
-    (200, 512, 264, 24),       # 2 slices of 4 stages, 13 token groups (the last of 8)
+    (200, 512, 264, 24),       # 8 stages would make only 2 slices: the plain path
     (256, 4096, 1024, 256),    # 16 slices, largest rank
     (257, 1024, 1024, 64),     # two token panels x 8 tiles: 4 slices of 4 stages
     (600, 1024, 520, 16),      # 3 ragged panels x 5 ragged tiles: 4 slices of 4 stages
@@ -150,7 +150,7 @@ SPLIT_DX = [
     (1, 512, 1000, 8),         # 4 slices of 4 stages, ragged last stage (1000 = 15 x 64 + 40)
     (16, 1024, 4096, 16),      # 16 slices of 4 stages
     (65, 4096, 4096, 64),      # 8 slices of 8 stages
-    (100, 2048, 520, 8),       # 2 slices (5 + 4 stages), ragged
+    (100, 2048, 520, 8),       # 9 stages would make only 2 slices: the plain path, ragged
     (200, 512, 2056, 24),      # 7 slices of 5 stages (the last of 3), 13 token groups
     (256, 1024, 4096, 256),    # 16 slices, largest rank
     (257, 1024, 4096, 64),     # two token panels x 8 tiles: 16 slices of 4 stages
