@@ -724,17 +724,54 @@ def bench_adamw_host_state(Q, torch, dev, iters, n=32 * 1024 * 1024):
     return {"params": n, "us_per_step": us, "host_link_GBps": 24 * n / (us * 1e-6) / 1e9}
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _blas_info():
+    """(name, threads) of the BLAS NumPy calls, from threadpoolctl when it is importable."""
+    try:
+        from threadpoolctl import threadpool_info
+
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                return f"{i.get('internal_api')} {i.get('version')}", i.get("num_threads")
+    except Exception:
+        pass
+    return None, None
+
+
 def cpu_baseline(M, din, dout, r, alpha, flops):
-    """The oracle as it stands: one step (dequantize + forward + backward) in float64 NumPy, the
-    weight quantized once beforehand."""
+    """The oracle as it stands, on the host cores.
+
+    value: one step of the headline workload (dequantize + forward + backward, the weight
+    quantized beforehand, as the GPU step), averaged over up to 5 repeats (about 10 s).
+    legs: every configuration once -- C1 (quantize + dequantize + forward + backward), C2
+    (the quantize alone), C3 both shapes in full, C4 (each 65B-shaped weight quantized and
+    dequantized once, then the forward at 1, 4 and 16 tokens), and C5 as an extrapolation:
+    one linear of each of its three shapes (quantize, dequantize, forward, backward at 2048
+    tokens; the 65B shapes reuse the C4 weights' quantize and dequantize times), one layer =
+    4 x (8192->8192) + 2 x (8192->22016) + 1 x (22016->8192), times 80."""
     import numpy as np
 
     import workloads
     from oracle import linear, nf4
 
+    def timed(fn):
+        t0 = time.perf_counter()
+        out = fn()
+        return out, time.perf_counter() - t0
+
     lin = workloads.Linear("proj", M, din, dout, r, alpha)
     inp = workloads.linear_inputs(2, lin)
-    q = nf4.quantize(inp.W, double_quant=True)
+    q, c2_quant_s = timed(lambda: nf4.quantize(inp.W, double_quant=True))
     reps, total = 0, 0.0
     while reps < 5 and (reps == 0 or total < 10.0):   # about 10 s of CPU work
         t0 = time.perf_counter()
@@ -744,17 +781,60 @@ def cpu_baseline(M, din, dout, r, alpha, flops):
         total += time.perf_counter() - t0
         reps += 1
     dt = total / reps
-    threads = None
-    try:
-        from threadpoolctl import threadpool_info
+    del Wd, q, inp
+    blas, blas_threads = _blas_info()
 
-        threads = max((i.get("num_threads", 0) for i in threadpool_info()), default=None)
-    except Exception:
-        pass
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads or len(os.sched_getaffinity(0)),
-            "kind": "oracle", "seconds_per_step": dt, "repeats": reps,
-            "sample": "full steps of the headline workload (dequantize + forward + backward), "
-                      "float64 NumPy, BLAS threads = cores, averaged over the repeats"}
+    def full(cfg, lin, backward=True):
+        """quantize + dequantize + forward (+ backward) of one linear, each part timed."""
+        li = workloads.linear_inputs(cfg, lin)
+        qq, tq = timed(lambda: nf4.quantize(li.W, double_quant=True))
+        wd, td = timed(lambda: nf4.dequantize(qq, (lin.d_out, lin.d_in)))
+        _, tf = timed(lambda: linear.forward(li.X, wd, li.A, li.B, lin.scale))
+        rec = {"quantize_s": tq, "dequant_s": td, "fwd_s": tf}
+        if backward:
+            _, tb = timed(lambda: linear.backward(li.dY, li.X, wd, li.A, li.B, lin.scale))
+            rec["bwd_s"] = tb
+        rec["total_s"] = sum(rec.values())
+        return rec, li, wd
+
+    legs = {}
+    rec, _, _ = full(1, workloads.CONFIGS[1].linears[0])
+    legs["C1"] = rec
+    legs["C2"] = {"quantize_s": c2_quant_s, "dequant_fwd_bwd_s": dt}
+    legs["C3"] = {l.name: full(3, l)[0] for l in workloads.CONFIGS[3].linears}
+    # C4: two distinct weights (one per orientation); the forward at each token count
+    c4, c5_parts = {}, {}
+    for nm, di, do in (("up", 8192, 22016), ("down", 22016, 8192)):
+        base = next(l for l in workloads.CONFIGS[4].linears if l.name == f"{nm}_M1")
+        rec, li, wd = full(4, base, backward=False)
+        for m in (1, 4, 16):
+            lm = workloads.Linear(f"{nm}_M{m}", m, di, do, 64, 16.0)
+            X = workloads.linear_inputs(4, lm, which=("X",)).X
+            _, tf = timed(lambda: linear.forward(X, wd, li.A, li.B, lm.scale))
+            c4[lm.name] = {"quantize_s": rec["quantize_s"], "dequant_s": rec["dequant_s"], "fwd_s": tf,
+                           "total_s": rec["quantize_s"] + rec["dequant_s"] + tf}
+        # the C5 linear of the same shape: forward + backward at 2048 tokens on this weight
+        l5 = workloads.Linear(nm, 2048, di, do, 64, 16.0)
+        t5 = workloads.linear_inputs(5, l5, which=("A", "B", "X", "dY"))
+        _, tf = timed(lambda: linear.forward(t5.X, wd, t5.A, t5.B, l5.scale))
+        _, tb = timed(lambda: linear.backward(t5.dY, t5.X, wd, t5.A, t5.B, l5.scale))
+        c5_parts[(di, do)] = rec["quantize_s"] + rec["dequant_s"] + tf + tb
+        del wd, li
+    legs["C4"] = c4
+    rec, _, _ = full(5, workloads.CONFIGS[5].linears[0])
+    c5_parts[(8192, 8192)] = rec["total_s"]
+    layer_s = 4 * c5_parts[(8192, 8192)] + 2 * c5_parts[(8192, 22016)] + c5_parts[(22016, 8192)]
+    legs["C5"] = {"extrapolated": True, "per_linear_s": {f"{a}->{b}": v for (a, b), v in c5_parts.items()},
+                  "layer_s": layer_s, "stack_80_layers_s": 80 * layer_s,
+                  "note": "one linear of each shape timed (quantize + dequantize + forward + backward, M = 2048); "
+                          "layer = 4 x 8192->8192 + 2 x 8192->22016 + 1 x 22016->8192; stack = 80 layers"}
+    cores = blas_threads or len(os.sched_getaffinity(0))
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "cpu_model": _cpu_model(), "blas": blas, "seconds_per_step": dt, "repeats": reps,
+            "sample": "value: full steps of the headline workload (dequantize + forward + backward; the weight "
+                      "quantized once before), float64 NumPy, BLAS threads = cores, averaged over the repeats; "
+                      "legs: every configuration timed once (C5 extrapolated from one linear per shape)",
+            "legs": legs}
 
 
 if __name__ == "__main__":

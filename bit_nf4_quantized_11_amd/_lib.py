@@ -5,7 +5,8 @@ import ctypes as C
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libqlora.so")
+# QLORA_LIB selects another build of the same sources (the sanitizer build, for example)
+LIB_PATH = os.environ.get("QLORA_LIB") or os.path.join(PKG, "libqlora.so")
 
 STATUS = {
     0: "QLORA_OK",
@@ -67,18 +68,31 @@ SIGNATURES = {
 _lib = None
 
 
+class StaleLibraryError(OSError):
+    """The built library's source hash differs from the sources in the package."""
+
+
 def load(build_if_missing: bool = True) -> C.CDLL:
-    """Load libqlora.so from the package directory (building it first if it is absent)."""
+    """Load libqlora.so from the package directory (building it first if it is absent).
+
+    A library built from other sources than the ones beside it is refused: its version
+    string carries the hash of the sources it was built from (see build.source_hash)."""
     global _lib
     if _lib is not None:
         return _lib
+    from . import build as _build
+
     if not os.path.exists(LIB_PATH):
         if not build_if_missing:
             raise OSError(f"libqlora.so is not built ({LIB_PATH})")
-        from . import build as _build
-
         _build.build()
     lib = C.CDLL(LIB_PATH)
+    lib.qlora_version.restype = C.c_char_p
+    version = lib.qlora_version().decode()
+    want = _build.source_hash()
+    if f"src {want}" not in version:
+        raise StaleLibraryError(f"{LIB_PATH} ({version}) was built from other sources than the current ones "
+                                f"(src {want}); rebuild with python -m bit_nf4_quantized_11_amd.build")
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)
         fn.restype = res

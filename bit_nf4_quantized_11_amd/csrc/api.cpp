@@ -292,7 +292,10 @@ const char* qlora_status_str(qlora_status s) {
   return "unknown status";
 }
 
-const char* qlora_version(void) { return "libqlora 0.1 (gfx950)"; }
+#ifndef QLORA_SOURCE_HASH
+#define QLORA_SOURCE_HASH "unknown"
+#endif
+const char* qlora_version(void) { return "libqlora 0.2 (gfx950, src " QLORA_SOURCE_HASH ")"; }
 
 qlora_status qlora_codebook_table(int32_t codebook, float levels[16], float thresholds[15]) {
   if (codebook < 0 || codebook >= kNumCodebooks) return QLORA_ERR_UNSUPPORTED;

@@ -1,6 +1,6 @@
 // Backward input gradient ("QLoRA: Efficient Finetuning of Quantized LLMs",
-// section "The QLoRA layer, end to end": the gradient passes through the frozen
-// weight, which forces a second dequantization on the backward pass):
+// section "The QLoRA layer, end to end": the input gradient is a product with the
+// transposed frozen weight, so the 4-bit weight is decoded a second time in the backward):
 //
 //   dX[M][K] = bf16( dY[M][N] deq(W) + Gs[M][rp] A~^T ),  A~(k, j) = A[k][j] (j < r), 0 otherwise
 //

@@ -1,6 +1,7 @@
 // Fused forward for large token counts ("QLoRA: Efficient Finetuning of Quantized
-// LLMs", section "The QLoRA layer, end to end": the weight is dequantized to bf16
-// on the fly, used, and thrown away; y = x W + s (x L1) L2):
+// LLMs", section "The QLoRA layer, end to end": every product runs in bf16 on a
+// weight decoded from its 4-bit storage, and no bf16 copy of the weight is kept;
+// y = x W + s (x L1) L2):
 //
 //   Y[M][N] = bf16( X[M][K] deq(W)^T + Ts[M][rp] B~ ),   B~(j, n) = B[j][n] (j < r), 0 otherwise
 //

@@ -1,7 +1,7 @@
 // Forward for few tokens (M <= 64), where the layer is bound by streaming the
 // packed weight from HBM ("QLoRA: Efficient Finetuning of Quantized LLMs",
-// section "The QLoRA layer, end to end": the weight is dequantized to bf16 on the
-// fly, used, and thrown away; y = x W + s (x L1) L2).
+// section "The QLoRA layer, end to end": the products run in bf16 on a weight
+// decoded from 4-bit storage in registers, never written back; y = x W + s (x L1) L2).
 //
 // Two launches:
 //   k_fwd_nf4_gemv      one grid of two kinds of workgroups:

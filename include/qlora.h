@@ -60,7 +60,9 @@ typedef enum {
  *            group holds element i in bits 3..0 and element i+4 in bits 7..4 (so every
  *            64 elements take 32 bytes whatever B).  Positions past the end of the
  *            tensor hold the code of the table's exact zero (7 for NF4, 8 for FP4 and
- *            INT4).
+ *            INT4).  (Not "two adjacent elements per byte": with this order one mask
+ *            gives four codes in element order and a shift plus mask the other four,
+ *            each ready for the byte-permute table lookup of the kernels.)
  *   absmax : double_quant = 1 -> nblk bytes, FP8 E4M3 code of (absmax_b - mu) / c1
  *            (OCP e4m3fn: the quantizer writes magnitudes up to 448; the codes 0x7F
  *            and 0xFF are NaN and give NaN weights if a caller stores them)
@@ -90,7 +92,9 @@ typedef struct {
 /* Human-readable name of a status code (static string). */
 const char* qlora_status_str(qlora_status s);
 
-/* Library version string (static). */
+/* Library version string (static): "libqlora <version> (gfx950, src <hash>)", where
+ * <hash> identifies the sources the library was built from (16 hex digits of a sha256
+ * over the sources, this header and the compile flags).                            */
 const char* qlora_version(void);
 
 /* Host only.  The 16 NF4 levels (fp32, ascending; index 7 is the exact zero)
@@ -155,12 +159,13 @@ qlora_status qlora_dequant(const qlora_nf4* w, uint16_t* W_out, hipStream_t stre
 
 /* Forward ("The QLoRA layer, end to end"):
  *   Y [M][out] = bf16( X [M][in] deq(W)^T + scale * T B ),  T = X A  [M][r]
- * The dequantized weight is formed on the fly and never stored.  T is rounded
+ * The bf16 weight is decoded inside the kernels and never written out.  T is rounded
  * to bf16 before its product with B.  If T_save is not NULL, bf16(T) is written
  * there [M][r] for the backward.  M >= 0; M = 0 is a no-op, and then the token
  * buffers X, Y and T_save may be NULL.
  * Requires: in % 64 == 0 and in % block_size == 0 (blocks lie inside weight rows),
- * out % 8 == 0, r % 8 == 0, 8 <= r <= 256; all pointers 16-byte aligned; ws of
+ * out % 8 == 0 (rows of B, dY and Y are moved as 16-byte vectors of 8 bf16),
+ * r % 8 == 0, 8 <= r <= 256; all pointers 16-byte aligned; ws of
  * qlora_fwd_workspace(M, in, out, r) bytes.                                     */
 qlora_status qlora_linear_fwd(const uint16_t* X, int64_t M, const qlora_nf4* w, const uint16_t* A,
                               const uint16_t* B, int32_t r, float scale, uint16_t* Y, uint16_t* T_save,

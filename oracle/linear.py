@@ -29,21 +29,32 @@ def _f64(u16) -> np.ndarray:
 
 
 def forward(X, Wq, A, B, s: float):
-    """Returns (Y [M][out], T = X A [M][r]) in float64."""
+    """Returns (Y [M][out], T = X A [M][r]) in float64.
+
+    The layer output is the frozen product plus the scaled rank-r path; T is the
+    rank-r activation, returned because the backward needs it."""
     x, w, a, b = _f64(X), _f64(Wq), _f64(A), _f64(B)
     t = x @ a
-    y = x @ w.T + s * (t @ b)
-    return y, t
+    base = x @ w.T
+    return base + s * (t @ b), t
 
 
 def backward(dY, X, Wq, A, B, s: float):
-    """Returns (dX [M][in], dA [in][r], dB [r][out]) in float64."""
+    """Returns (dX [M][in], dA [in][r], dB [r][out]) in float64.
+
+    Chain rule on L = <Y, dY> with Y = X Wq^T + s (X A) B:
+      - Y depends on X through Wq^T and through A then B, so dL/dX is dY Wq plus
+        s (dY B^T) A^T;
+      - Y depends on A only through the product X A, whose gradient is s dY B^T,
+        so dL/dA = X^T (s dY B^T);
+      - Y depends on B through (X A) B, so dL/dB = s (X A)^T dY;
+      - the frozen Wq gets no gradient."""
     dy, x, w, a, b = _f64(dY), _f64(X), _f64(Wq), _f64(A), _f64(B)
-    g = dy @ b.T                    # dY L2^T
-    dx = dy @ w + s * (g @ a.T)     # passes through the frozen weight
-    da = s * (x.T @ g)
-    db = s * ((x @ a).T @ dy)
-    return dx, da, db
+    up = dy @ b.T                           # gradient reaching the rank-r activation, before s
+    grad_x = dy @ w + s * (up @ a.T)
+    grad_a = s * (x.T @ up)
+    grad_b = s * ((x @ a).T @ dy)
+    return grad_x, grad_a, grad_b
 
 
 def forward_rows(X, Wq, A, B, s: float, rows):

@@ -195,3 +195,12 @@ def test_status_strings(lib):
     for s in range(7):
         assert lib.qlora_status_str(s)
     assert b"gfx950" in lib.qlora_version()
+
+
+def test_version_names_the_sources_it_was_built_from(lib):
+    """The loaded library's version string carries the hash of the current sources
+    (the loader refuses a library built from other sources)."""
+    from bit_nf4_quantized_11_amd import build
+
+    v = lib.qlora_version().decode()
+    assert f"src {build.source_hash()})" in v, v

@@ -128,6 +128,7 @@ SPLIT_FWD = [
     (100, 1024, 520, 8),
     (128, 2048, 1000, 16),
     (200, 512, 264, 24),       # 8 stages would make only 2 slices: the plain path
+    (128, 768, 1000, 16),      # 8 tiles, 12 stages: exactly 3 slices of 4 (the smallest split)
     (256, 4096, 1024, 256),    # 16 slices, largest rank
     (257, 1024, 1024, 64),     # two token panels x 8 tiles: 4 slices of 4 stages
     (600, 1024, 520, 16),      # 3 ragged panels x 5 ragged tiles: 4 slices of 4 stages
@@ -151,6 +152,7 @@ SPLIT_DX = [
     (16, 1024, 4096, 16),      # 16 slices of 4 stages
     (65, 4096, 4096, 64),      # 8 slices of 8 stages
     (100, 2048, 520, 8),       # 9 stages would make only 2 slices: the plain path, ragged
+    (100, 1024, 720, 8),       # 8 tiles, 12 stages: exactly 3 slices of 4, ragged last stage
     (200, 512, 2056, 24),      # 7 slices of 5 stages (the last of 3), 13 token groups
     (256, 1024, 4096, 256),    # 16 slices, largest rank
     (257, 1024, 4096, 64),     # two token panels x 8 tiles: 16 slices of 4 stages
@@ -278,60 +280,52 @@ def test_c2_full():
     _check_full(workloads.linear_inputs(2, lin), label="C2")
 
 
-def _check_sampled(cfg, lin, rows, backward=True, layer=0):
-    """Full-size run; Y/dX checked on sampled token rows, dA/dB in full."""
-    inp = workloads.linear_inputs(cfg, lin, layer=layer)
-    log("linear sampled", lin.name, f"M={lin.M} in={lin.d_in} out={lin.d_out}")
-    g = _run(inp, backward=backward)
-    Wd = _oracle_weight(inp.W, (lin.d_out, lin.d_in))
-    rows = np.asarray(rows)
-    y = linear.forward_rows(inp.X, Wd, inp.A, inp.B, lin.scale, rows)
-    assert_close(host(g["Y"].float())[rows], y, f"{lin.name} Y rows")
-    if backward:
-        dx = linear.backward_dx_rows(inp.dY, Wd, inp.A, inp.B, lin.scale, rows)
-        assert_close(host(g["dX"].float())[rows], dx, f"{lin.name} dX rows")
-        x, a, b, dy = bf16_f64(inp.X), bf16_f64(inp.A), bf16_f64(inp.B), bf16_f64(inp.dY)
-        gm = dy @ b.T
-        assert_close(host(g["dA"]), lin.scale * (x.T @ gm), f"{lin.name} dA")
-        assert_close(host(g["dB"]), lin.scale * ((x @ a).T @ dy), f"{lin.name} dB")
-
-
 @pytest.mark.parametrize("which", [0, 1])
-def test_c3_full_sampled(which):
+def test_c3_full(which):
+    """7B MLP shapes with outliers, 4096 tokens: every element of Y, T, dX, dA, dB."""
     lin = workloads.CONFIGS[3].linears[which]
-    rows = np.random.default_rng(which).choice(lin.M, 192, replace=False)
-    _check_sampled(3, lin, rows)
+    _check_full(workloads.linear_inputs(3, lin), label=f"C3 {lin.name}")
+
+
+# Oracle dequantized weights of the two 65B shapes, shared by the skinny cases (the six
+# configurations and the 64-token runs draw the same two weights).
+_W65 = {}
+
+
+def _oracle_weight_65b(inp):
+    lin = inp.spec
+    key = (lin.d_out, lin.d_in)
+    if key not in _W65:
+        log("oracle quantize", key)
+        _W65[key] = _oracle_weight(inp.W, key)
+    return _W65[key]
+
+
+def _check_skinny_65b(inp):
+    """Skinny forward at a 65B shape: Y and T on every token and column."""
+    lin = inp.spec
+    log("skinny", lin.name, f"M={lin.M} in={lin.d_in} out={lin.d_out}")
+    g = _run(inp, backward=False)
+    Wd = _oracle_weight_65b(inp)
+    y, t = linear.forward(inp.X, Wd, inp.A, inp.B, lin.scale)
+    assert_close(host(g["Y"].float()), y, f"{lin.name} Y")
+    assert_close(host(g["T"].float()), t, f"{lin.name} T")
 
 
 @pytest.mark.parametrize("idx", range(6))
 def test_c4_skinny_full(idx):
-    """Skinny forward at 65B shapes; every token row checked, on sampled output columns."""
+    """Skinny forward at 65B shapes, M in {1, 4, 16}: every output checked."""
     require_gpu()
     lin = workloads.CONFIGS[4].linears[idx]
-    _check_skinny_columns(workloads.linear_inputs(4, lin), idx)
+    _check_skinny_65b(workloads.linear_inputs(4, lin))
 
 
 @pytest.mark.parametrize("which", [0, 1])
 def test_skinny_64_tokens_65b_shapes(which):
-    """64 tokens (four groups of 16) at the 65B shapes, on sampled output columns."""
+    """64 tokens (four groups of 16) on the 65B-shaped weights: every output checked."""
     require_gpu()
-    din, dout = ((8192, 22016), (22016, 8192))[which]
-    _check_skinny_columns(workloads.custom_linear(64, din, dout, 64, seed=640 + which, alpha=16.0), 10 + which)
-
-
-def _check_skinny_columns(inp, idx):
-    lin = inp.spec
-    log("skinny", lin.name, f"M={lin.M} in={lin.d_in} out={lin.d_out}")
-    g = _run(inp, backward=False)
-    cols = np.sort(np.random.default_rng(idx).choice(lin.d_out, 96, replace=False))
-    # oracle weight rows for the sampled columns only (the constants need every block)
-    absmax = nf4.blockwise_absmax(inp.W)
-    c2, c1, mu = nf4.double_quantize(absmax)
-    scales = nf4.block_scales_dq(c2, c1, mu)
-    nkb = lin.d_in // 64
-    blocks = (cols[:, None] * nkb + np.arange(nkb)[None, :]).reshape(-1)
-    codes = nf4.codes_for_blocks(inp.W, absmax, blocks).reshape(-1)
-    wrows = nf4.dequantize_codes(codes, scales[blocks]).reshape(cols.size, lin.d_in)
-    x, a, b = bf16_f64(inp.X), bf16_f64(inp.A), bf16_f64(inp.B)
-    y = x @ bf16_f64(wrows).T + lin.scale * (x @ a) @ b[:, cols]
-    assert_close(host(g["Y"].float())[:, cols], y, f"{lin.name} Y cols")
+    lin = workloads.CONFIGS[4].linears[which]
+    inp = workloads.linear_inputs(4, lin)
+    big = workloads.Linear(f"{lin.name}_M64", 64, lin.d_in, lin.d_out, lin.r, lin.alpha)
+    X = workloads.normal_bf16(workloads.seed_for(4, 1, workloads.TID_X), (64, lin.d_in), 1.0)
+    _check_skinny_65b(workloads.LinearInputs(inp.W, inp.A, inp.B, X, None, big))
