@@ -181,6 +181,18 @@ def qlora_linear_fwd(X: torch.Tensor, w: NF4Weight, A: torch.Tensor, B: torch.Te
     return Y, (T_save if save_T else None)
 
 
+def qlora_linear_fwd_noalloc(X: torch.Tensor, w: NF4Weight, A: torch.Tensor, B: torch.Tensor, scale: float,
+                             Y: torch.Tensor, T_save: torch.Tensor | None = None, stream=None):
+    """The forward with the library's own scratch array (no workspace, nothing allocated);
+    Y (and T_save, if given) must be allocated by the caller.  Returns (Y, T_save)."""
+    _bf16(X, "X"); _bf16(A, "A"); _bf16(B, "B")
+    d = w.desc()
+    _check(lib().qlora_linear_fwd_noalloc(_ptr(X), X.shape[0], C.byref(d), _ptr(A), _ptr(B), A.shape[1],
+                                          float(scale), _ptr(Y), _ptr(T_save), _stream(stream)),
+           "qlora_linear_fwd_noalloc")
+    return Y, T_save
+
+
 def qlora_linear_bwd(dY: torch.Tensor, X: torch.Tensor, T_saved: torch.Tensor | None, w: NF4Weight,
                      A: torch.Tensor, B: torch.Tensor, scale: float, need_dX: bool = True,
                      dX: torch.Tensor | None = None, dA: torch.Tensor | None = None, dB: torch.Tensor | None = None,

@@ -8,6 +8,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 # QLORA_LIB selects another build of the same sources (the sanitizer build, for example)
 LIB_PATH = os.environ.get("QLORA_LIB") or os.path.join(PKG, "libqlora.so")
 
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024   # QLORA_NOALLOC_SCRATCH_BYTES in qlora.h
+
 STATUS = {
     0: "QLORA_OK",
     1: "QLORA_ERR_NULL",
@@ -58,6 +60,8 @@ SIGNATURES = {
     "qlora_dequant": (C.c_int, [C.POINTER(qlora_nf4), C.c_void_p, C.c_void_p]),
     "qlora_linear_fwd": (C.c_int, [C.c_void_p, C.c_int64, C.POINTER(qlora_nf4), C.c_void_p, C.c_void_p, C.c_int32,
                                    C.c_float, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "qlora_linear_fwd_noalloc": (C.c_int, [C.c_void_p, C.c_int64, C.POINTER(qlora_nf4), C.c_void_p, C.c_void_p,
+                                           C.c_int32, C.c_float, C.c_void_p, C.c_void_p, C.c_void_p]),
     "qlora_linear_bwd": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64, C.POINTER(qlora_nf4), C.c_void_p,
                                    C.c_void_p, C.c_int32, C.c_float, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                    C.c_size_t, C.c_void_p]),

@@ -277,6 +277,22 @@ QuantWs quant_layout(void* base, int64_t numel, int block) {
 
 }  // namespace
 
+namespace qlora {
+// Argument checks of the forward (everything except the workspace), shared with the entry
+// point that brings its own scratch memory.
+qlora_status linear_fwd_check(const uint16_t* X, int64_t M, const qlora_nf4* w, const uint16_t* A, const uint16_t* B,
+                              int32_t r, const uint16_t* Y, const uint16_t* T_save) {
+  const qlora_status st = check_linear(M, w, r);
+  if (st != QLORA_OK) return st;
+  // with no tokens the token buffers may be NULL (e.g. empty tensors)
+  if (!A || !B || (M > 0 && (!X || !Y))) return QLORA_ERR_NULL;
+  if ((X && !aligned16(X)) || !aligned16(A) || !aligned16(B) || (Y && !aligned16(Y)) ||
+      (T_save && !aligned16(T_save)))
+    return QLORA_ERR_ALIGN;
+  return QLORA_OK;
+}
+}  // namespace qlora
+
 extern "C" {
 
 const char* qlora_status_str(qlora_status s) {
@@ -380,13 +396,8 @@ qlora_status qlora_dequant(const qlora_nf4* w, uint16_t* W_out, hipStream_t stre
 qlora_status qlora_linear_fwd(const uint16_t* X, int64_t M, const qlora_nf4* w, const uint16_t* A,
                               const uint16_t* B, int32_t r, float scale, uint16_t* Y, uint16_t* T_save, void* ws,
                               size_t ws_bytes, hipStream_t stream) {
-  qlora_status st = check_linear(M, w, r);
+  const qlora_status st = qlora::linear_fwd_check(X, M, w, A, B, r, Y, T_save);
   if (st != QLORA_OK) return st;
-  // with no tokens the token buffers may be NULL (e.g. empty tensors)
-  if (!A || !B || (M > 0 && (!X || !Y))) return QLORA_ERR_NULL;
-  if ((X && !aligned16(X)) || !aligned16(A) || !aligned16(B) || (Y && !aligned16(Y)) ||
-      (T_save && !aligned16(T_save)))
-    return QLORA_ERR_ALIGN;
   const int64_t in = w->cols, out = w->rows, rp = rank_pad(r);
   const FwdWs need = fwd_layout(nullptr, M, in, out, r);
   if (!ws || ws_bytes < need.bytes) return QLORA_ERR_WORKSPACE;

@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include "common.h"
+#include "qlora.h"
 
 namespace qlora {
 
@@ -17,6 +18,10 @@ constexpr int kNumCodebooks = 3;   // NF4, FP4, INT4
 const float* codebook_levels_host(int which);
 const float* codebook_thresholds_host(int which);
 NF4Table nf4_table(int which);
+
+// Argument checks of qlora_linear_fwd other than the workspace (api.cpp).
+qlora_status linear_fwd_check(const uint16_t* X, int64_t M, const qlora_nf4* w, const uint16_t* A, const uint16_t* B,
+                              int32_t r, const uint16_t* Y, const uint16_t* T_save);
 
 // Optional per-launch timing (api.cpp).
 struct ProfScope {

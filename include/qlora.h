@@ -183,6 +183,20 @@ qlora_status qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, const uint1
                               const qlora_nf4* w, const uint16_t* A, const uint16_t* B, int32_t r, float scale,
                               uint16_t* dX, float* dA, float* dB, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* The forward of qlora_linear_fwd with no workspace argument and no allocation, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, results (bit for bit) and rules as
+ * qlora_linear_fwd; the scratch memory is a fixed array of QLORA_NOALLOC_SCRATCH_BYTES that
+ * the library holds on every GPU it runs on until the process ends.  Returns
+ * QLORA_ERR_WORKSPACE (and launches nothing) when qlora_fwd_workspace(M, in, out, r) exceeds
+ * that size.  Calls that overlap in time on one GPU (several streams or host threads) share
+ * the array and race: the caller serializes them.  The first call on each device takes the
+ * array's device address (hipGetSymbolAddress) with that device current.                */
+#define QLORA_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+qlora_status qlora_linear_fwd_noalloc(const uint16_t* X, int64_t M, const qlora_nf4* w, const uint16_t* A,
+                                      const uint16_t* B, int32_t r, float scale, uint16_t* Y, uint16_t* T_save,
+                                      hipStream_t stream);
+
 /* Merge the adapter into the base weight ("QLoRA: quantising the part you are not
  * training", section "What it costs": merging into the quantised base means
  * requantising): W_out [out][in] bf16 with
