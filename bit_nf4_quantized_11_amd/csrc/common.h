@@ -72,6 +72,8 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // architecture; every E4M3 value is exact in fp32).  A test dequantizes a weight whose
 // block constants run through all 256 codes and compares with the definition.
 __device__ __forceinline__ float e4m3_decode(uint32_t c) { return __builtin_amdgcn_cvt_f32_fp8((int)c, 0); }
+// the code in byte 1 of c
+__device__ __forceinline__ float e4m3_decode_byte1(uint32_t c) { return __builtin_amdgcn_cvt_f32_fp8((int)c, 1); }
 
 // Round-to-nearest-even encode; magnitudes above 448 clamp to 448 (never reached
 // by the quantizer, whose values stay within 448 * (1 + 2^-22)).
@@ -135,21 +137,26 @@ __device__ __forceinline__ Planes make_planes(const NF4Table& t, float s) {
   return p;
 }
 
-// Four codes (bytes of idx, each 0..15) -> two dwords of bf16 pairs, in order
-// {val[idx.b0], val[idx.b1]} and {val[idx.b2], val[idx.b3]}.
-__device__ __forceinline__ void lookup4(const Planes& p, uint32_t idx, uint32_t& d0, uint32_t& d1) {
-  uint32_t sel = idx & 0x07070707u;
-  // 0xFF in each byte whose code is >= 8: v_perm selectors 13..20 give 0xFF, 5..12 give 0x00
-  // when both sources are zero.
-  uint32_t mask = __builtin_amdgcn_perm(0u, 0u, idx + 0x05050505u);
-  uint32_t lo_a = __builtin_amdgcn_perm(p.lo[1], p.lo[0], sel);
-  uint32_t lo_b = __builtin_amdgcn_perm(p.lo[3], p.lo[2], sel);
-  uint32_t hi_a = __builtin_amdgcn_perm(p.hi[1], p.hi[0], sel);
-  uint32_t hi_b = __builtin_amdgcn_perm(p.hi[3], p.hi[2], sel);
-  uint32_t lo = (lo_b & mask) | (lo_a & ~mask);
-  uint32_t hi = (hi_b & mask) | (hi_a & ~mask);
+// Four codes -> two dwords of bf16 pairs, in order {val[c0], val[c1]} and {val[c2], val[c3]}.
+// sel holds the low three bits of each code (one per byte), mask is 0xFF in each byte
+// whose code is 8 or more: entries 0..7 and 8..15 are looked up separately (v_perm_b32
+// selects a byte out of an 8-byte pair) and merged on the mask.
+__device__ __forceinline__ void lookup4(const Planes& p, uint32_t sel, uint32_t mask, uint32_t& d0, uint32_t& d1) {
+  const uint32_t lo_a = __builtin_amdgcn_perm(p.lo[1], p.lo[0], sel);
+  const uint32_t lo_b = __builtin_amdgcn_perm(p.lo[3], p.lo[2], sel);
+  const uint32_t hi_a = __builtin_amdgcn_perm(p.hi[1], p.hi[0], sel);
+  const uint32_t hi_b = __builtin_amdgcn_perm(p.hi[3], p.hi[2], sel);
+  const uint32_t lo = (lo_b & mask) | (lo_a & ~mask);
+  const uint32_t hi = (hi_b & mask) | (hi_a & ~mask);
   d0 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
   d1 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+}
+
+// 0xFF in byte j of the result where bit 7 of byte j of x is set.  v_perm_b32 selectors
+// 8..11 replicate bit 7 of bytes 1, 3, 5 and 7 of its 8-byte input {S0, S1}; with S1 = x
+// and S0 = x << 8 those are bytes 1, 3, 0 and 2 of x.
+__device__ __forceinline__ uint32_t top_bit_mask(uint32_t x) {
+  return __builtin_amdgcn_perm(x << 8, x, 0x090B080Au);
 }
 
 // One code dword = 8 weights of a group; byte i holds element i in bits 3..0 and
@@ -157,8 +164,9 @@ __device__ __forceinline__ void lookup4(const Planes& p, uint32_t idx, uint32_t&
 __device__ __forceinline__ u32x4 dequant8(const Planes& p, uint32_t codes) {
   u32x4 o;
   uint32_t a, b, c, d;
-  lookup4(p, codes & 0x0F0F0F0Fu, a, b);
-  lookup4(p, (codes >> 4) & 0x0F0F0F0Fu, c, d);
+  // low nibbles: bit 3 of each byte moves to bit 7 with a shift by 4
+  lookup4(p, codes & 0x07070707u, top_bit_mask(codes << 4), a, b);
+  lookup4(p, (codes >> 4) & 0x07070707u, top_bit_mask(codes), c, d);
   o.x = a; o.y = b; o.z = c; o.w = d;
   return o;
 }

@@ -49,11 +49,11 @@ constexpr int ACH = 64;           // rows of A per LDS chunk (8 KiB)
 constexpr int XAS = 72;           // X chunk row stride in the adapter workgroups (64 + 8 padding)
 constexpr int KA = 2048;          // rows of A per adapter slice
 constexpr int kSlotsPerCU = 2;    // resident workgroups per CU the grid is sized for (TG = 1)
-constexpr int RING = 4;           // row groups of packed weight in flight per wave
+constexpr int RG_ROUND = 4;       // row groups x token groups per round (one LDS hand-over each)
 
-// LDS: weight groups use two [TG][8 waves][64 lanes] float4 tiles; adapter groups two A
-// chunks, two X chunks and the [4][64] float4 hand-over area of waves 4..7.
-constexpr size_t kLdsWeight = 2 * 8 * 64 * 16;   // per token group
+// LDS: weight groups use two buffers of RG_ROUND [8 waves][64 lanes] float4 tiles; adapter
+// groups two A chunks, two X chunks and the [4][64] float4 hand-over area of waves 4..7.
+constexpr size_t kLdsWeight = 2 * RG_ROUND * 8 * 64 * 16;
 constexpr size_t kLdsAdapter = 2 * ACH * 64 * 2 + 2 * 16 * XAS * 2 + 4 * 64 * 16;
 
 struct GemvParams {
@@ -90,7 +90,7 @@ __device__ __forceinline__ int apos(int k, int q) {
 // a block), 2 for 32 (two blocks per lane: two constants and two tables).
 template <bool DQ, int BM, int TG>
 __device__ __forceinline__ void weight_group(const GemvParams& p, int bid, uint8_t* lds) {
-  float4* const red = reinterpret_cast<float4*>(lds);          // [2][TG][8][64]
+  float4* const red = reinterpret_cast<float4*>(lds);          // [2][RG_ROUND][8][64]
   const int rranges = (int)p.rranges;
   const int slice = bid / rranges, rr = bid - slice * rranges;
   const int64_t G = p.rgroups;
@@ -131,9 +131,11 @@ __device__ __forceinline__ void weight_group(const GemvParams& p, int bid, uint8
 
   struct WStep {
     uint4 c0, c1;     // the 32 code bytes of the lane's 64 weights
-    uint32_t c2;      // 8-bit block constant (double quant) or fp32 absmax bits; for blocks
-                      // of 32 the two constants (two bytes, or the first fp32)
-    uint32_t c2b;     // blocks of 32 without double quant: the second fp32 absmax
+    uint32_t c2;      // double quant: the aligned dword holding the lane's 8-bit block
+                      // constant (blocks of 32: both constants); else the fp32 absmax bits
+                      // (blocks of 32: the first)
+    uint32_t c2b;     // double quant: bit offset of the constant in c2; blocks of 32
+                      // without double quant: the second fp32 absmax
     float c1f;        // group scale
   };
   const uint32_t bsh = (uint32_t)(p.w.bshift - 6);   // BM == 1: 64-chunks per block, log2
@@ -147,12 +149,12 @@ __device__ __forceinline__ void weight_group(const GemvParams& p, int bid, uint8
     // first block of the chunk (blocks of 32: blocks 2 blk and 2 blk + 1, one group of 256)
     const uint32_t sb = BM == 0 ? blk : BM == 1 ? blk >> bsh : blk << 1;
     if constexpr (dq) {
-      if constexpr (BM == 2)
-        S.c2 = __builtin_amdgcn_raw_buffer_load_b16(rA, sb, 0, 0);
-      else
-        S.c2 = __builtin_amdgcn_raw_buffer_load_b8(rA, sb, 0, 0);
+      // a whole dword (the constants buffer holds a multiple of 4 bytes for every weight the
+      // linear calls take): a byte-sized load would be carried between rounds as a narrow
+      // value that the compiler widens right after the load, waiting for it there
+      S.c2 = __builtin_amdgcn_raw_buffer_load_b32(rA, sb & ~3u, 0, 0);
+      S.c2b = (sb & 3u) * 8u;
       S.c1f = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rC1, (sb >> 8) * 4, 0, 0));
-      S.c2b = 0;
     } else {
       if constexpr (BM == 2) {
         S.c2 = __builtin_amdgcn_raw_buffer_load_b32(rA, sb * 4, 0, 0);
@@ -164,32 +166,53 @@ __device__ __forceinline__ void weight_group(const GemvParams& p, int bid, uint8
       S.c1f = 0.0f;
     }
   };
-  // reduction of the tiles: thread t sums element (row t % 16, token (t % 256) / 16) of the
-  // eight waves' tiles of token groups t / 256, t / 256 + 2, .., in wave order; acc[v] of
-  // lane l holds row 4 (l / 16) + v, token l % 16
-  const int rrow = t & 15, rtok = (t & 255) >> 4;
-  const int roff = ((rrow >> 2) * 16 + rtok) * 4 + (rrow & 3);
-  float* const pout = p.partial + ((int64_t)slice * p.M + rtok) * p.npad + rrow;
-  // The scheduling barriers and the empty asm keep each step's work inside its step: left
-  // free, the compiler moves arithmetic on the next step's freshly loaded codes ahead and
-  // so waits for loads issued a moment earlier.
-  auto step = [&](int i, const WStep& S) {
+  // The wave works in rounds of R row groups (R x TG accumulator tiles), loading the codes
+  // of the next round while it computes this one, and the eight waves' tiles meet in LDS
+  // once per round.  acc[v] of lane l holds row 4 (l / 16) + v, token l % 16 of a tile.
+  constexpr int R = RG_ROUND / TG;
+  constexpr int TILES = R * TG;                                  // tiles per wave and round
+  // reduction mapping: thread t sums rows t % 16 of tokens (t / 16) % 16 of tiles t / 256,
+  // t / 256 + 2, ... (so a wave stores 64 consecutive rows of four tokens)
+  const int rrow = t & 15, rtok = (t >> 4) & 15, rt0 = t >> 8;
+  const int roff = ((rrow >> 2) * 16 + rtok) * 4 + (rrow & 3);   // float offset inside a tile
+  // partials through a buffer resource: an offset past its end drops the store, so the
+  // reduction needs no branch (a branch around the stores would make the compiler lose track
+  // of the loads in flight and wait for all of them at the next round)
+  const uint32_t pbytes = (uint32_t)(p.splits * p.M * p.npad * 4);
+  const rsrc_t rP = make_rsrc(p.partial, pbytes);
+  const uint32_t pbase = (uint32_t)((slice * p.M + rtok) * p.npad + rrow) * 4u;
+  // one row group: dequantize the lane's block, TG x 8 MFMAs.  The scheduling barriers and the
+  // empty asm keep each row group's work in place: left free, the compiler moves arithmetic
+  // on the next round's freshly loaded codes ahead and so waits for loads issued a moment
+  // earlier.
+  auto step = [&](const WStep& S, f32x4 (&acc)[TG]) {
     __builtin_amdgcn_sched_barrier(0);
-    const float sc = dq ? __fadd_rn(__fmul_rn(e4m3_decode(S.c2 & 0xFFu), S.c1f), mu) : __uint_as_float(S.c2);
     u32x4 q0 = {S.c0.x, S.c0.y, S.c0.z, S.c0.w}, q1 = {S.c1.x, S.c1.y, S.c1.z, S.c1.w};
-    asm volatile("" : "+v"(q0), "+v"(q1));
+    uint32_t c2 = S.c2, c2b = S.c2b;
+    float c1f = S.c1f;
+    asm volatile("" : "+v"(q0), "+v"(q1), "+v"(c2), "+v"(c2b), "+v"(c1f));
+    if constexpr (dq) c2 >>= c2b;
+    // v_cvt_f32_fp8 reads byte 0 of its operand (the lane's constant; blocks of 32: the first)
+    const float sc = dq ? __fadd_rn(__fmul_rn(e4m3_decode(c2), c1f), mu) : __uint_as_float(c2);
     const Planes pl = make_planes(p.tab, kvalid ? sc : 0.0f);
     const uint32_t cw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-    f32x4 acc[TG];
 #pragma unroll
     for (int tg = 0; tg < TG; ++tg) acc[tg] = f32x4{0.f, 0.f, 0.f, 0.f};
     if constexpr (BM == 2) {
-      // code words 0..3 hold the first block of 32, 4..7 the second
-      const float sc2 = dq ? __fadd_rn(__fmul_rn(e4m3_decode(S.c2 >> 8), S.c1f), mu) : __uint_as_float(S.c2b);
+      // code words 0..3 hold the first block of 32, 4..7 the second (its table is built once
+      // the first one is done with, so the two never occupy registers together)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const u32x4 wv = dequant8(pl, cw[c]);
+#pragma unroll
+        for (int tg = 0; tg < TG; ++tg) acc[tg] = mfma16(wv, xr[tg][c], acc[tg]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      const float sc2 = dq ? __fadd_rn(__fmul_rn(e4m3_decode_byte1(c2), c1f), mu) : __uint_as_float(c2b);
       const Planes pl2 = make_planes(p.tab, kvalid ? sc2 : 0.0f);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const u32x4 wv = dequant8(c < 4 ? pl : pl2, cw[c]);
+      for (int c = 4; c < 8; ++c) {
+        const u32x4 wv = dequant8(pl2, cw[c]);
 #pragma unroll
         for (int tg = 0; tg < TG; ++tg) acc[tg] = mfma16(wv, xr[tg][c], acc[tg]);
       }
@@ -201,41 +224,80 @@ __device__ __forceinline__ void weight_group(const GemvParams& p, int bid, uint8
         for (int tg = 0; tg < TG; ++tg) acc[tg] = mfma16(wv, xr[tg][c], acc[tg]);
       }
     }
-    float4* const buf = red + (i & 1) * (512 * TG);
-#pragma unroll
-    for (int tg = 0; tg < TG; ++tg)
-      buf[tg * 512 + wave * 64 + lane] = make_float4(acc[tg][0], acc[tg][1], acc[tg][2], acc[tg][3]);
-    __syncthreads();
-    const int n = (rg_beg + i) * RGR + rrow;
-#pragma unroll
-    for (int tg = 0; tg < TG; ++tg) {
-      if ((t >> 8) == (tg & 1) && tg * 16 + rtok < M && n < N) {
-        const float* b = reinterpret_cast<const float*>(buf + tg * 512) + roff;
-        float sum = b[0];
-#pragma unroll
-        for (int w = 1; w < 8; ++w) sum = __fadd_rn(sum, b[w * 256]);
-        pout[(int64_t)tg * 16 * p.npad + (int64_t)(rg_beg + i) * RGR] = sum;
-      }
-    }
     __builtin_amdgcn_sched_barrier(0);
   };
-  // RING row groups in flight per wave (a ring of register sets); a load index past the end
-  // is clamped to the last row group (loaded again, never used)
-  WStep S[RING];
+  // eight waves' tiles of round q (row groups q R .. q R + R - 1) meet in LDS buffer q % 2
+  auto hand_over = [&](int q, const f32x4 (&acc)[R][TG]) {
+    const int g0 = q * R;
+    float4* const buf = red + (q & 1) * (TILES * 512);
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int tg = 0; tg < TG; ++tg)
+        buf[(r * TG + tg) * 512 + wave * 64 + lane] = make_float4(acc[r][tg][0], acc[r][tg][1], acc[r][tg][2],
+                                                                  acc[r][tg][3]);
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < TILES / 2; ++u) {
+      const int tile = rt0 + 2 * u, r = tile / TG, tg = tile - r * TG;
+      const int n = (rg_beg + g0 + r) * RGR + rrow;
+      const bool ok = g0 + r < n_it && tg * 16 + rtok < M && n < N;
+      const float* b = reinterpret_cast<const float*>(buf + tile * 512) + roff;
+      float sum = b[0];
+#pragma unroll
+      for (int w = 1; w < 8; ++w) sum = __fadd_rn(sum, b[w * 256]);
+      const uint32_t off = pbase + (uint32_t)(tg * 16 * p.npad + (rg_beg + g0 + r) * RGR) * 4u;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sum), rP, ok ? off : pbytes, 0, 0);
+    }
+  };
+  // Row groups are loaded RING ahead (a ring of register sets, one round of 4 row groups of
+  // work: RING / R rounds in flight), and a ring cycle runs without branches (a branch around a
+  // row group's work would make the compiler wait for every load in flight where it rejoins):
+  // the codes of row group i + RING are loaded right after row group i has used its registers.
+  // A load index past the end is clamped to the last row group (loaded again, never used).
+  constexpr int RING = 4;
+  static_assert(RING % R == 0, "whole rounds per ring cycle");
   const int last = max(n_it - 1, 0);
+  const int ncyc = n_it / RING;
+  WStep S[RING];
+  // the first loads in the order the loop issues them (slot by slot): the compiler's wait
+  // counts at the loop head must hold on entry as well as around the loop
 #pragma unroll
-  for (int d = 0; d < RING; ++d) load(min(d, last), S[d]);
-  int i = 0;
-  for (; i + RING - 1 < n_it; i += RING) {
+  for (int d = 0; d < RING; ++d) {
+    load(min(d, last), S[d]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int c = 0; c < ncyc; ++c) {
 #pragma unroll
-    for (int d = 0; d < RING; ++d) {
-      step(i + d, S[d]);
-      load(min(i + d + RING, last), S[d]);
+    for (int q = 0; q < RING / R; ++q) {
+      f32x4 acc[R][TG];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int d = q * R + r;
+        step(S[d], acc[r]);
+        load(min(c * RING + d + RING, last), S[d]);
+      }
+      hand_over(c * (RING / R) + q, acc);
     }
   }
+  // the last n_it % RING row groups (workgroup-uniform branches)
+  const int i0 = ncyc * RING;
 #pragma unroll
-  for (int d = 0; d < RING - 1; ++d)
-    if (i + d < n_it) step(i + d, S[d]);
+  for (int q = 0; q < RING / R; ++q) {
+    if (i0 + q * R < n_it) {
+      f32x4 acc[R][TG];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if (i0 + q * R + r < n_it) {
+          step(S[q * R + r], acc[r]);
+        } else {
+#pragma unroll
+          for (int tg = 0; tg < TG; ++tg) acc[r][tg] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+      hand_over(ncyc * (RING / R) + q, acc);
+    }
+  }
 }
 
 // ---- adapter workgroup: columns j0.. of A over a slice of KA rows; A is [K][r], columns
@@ -509,7 +571,7 @@ hipError_t launch_gemv(const uint16_t* X, int64_t M, int64_t K, int64_t N, const
   GemvParams p{X, M, K, N, w, nchunk * kBlockBytes, w.dq ? nblk : nblk * 4, w.dq ? ((nblk + 255) / 256) * 4 : 0,
                A, r, partial, partial + pl.tpart, pl.npad, pl.agroups * GROWS, pl.splits, pl.rgroups,
                pl.rranges, pl.agroups, pl.asplits, pl.ngr, nf4_table(w.cb)};
-  const size_t lds = std::max(kLdsWeight * pl.tg, kLdsAdapter);
+  const size_t lds = std::max(kLdsWeight, kLdsAdapter);
   ProfScope ps("k_fwd_nf4_gemv", s);
   const int64_t n_adapter = pl.agroups * pl.asplits * pl.ngr;
   const dim3 grid((unsigned)((adapters_only ? 0 : pl.rranges * pl.splits) + n_adapter));
