@@ -245,6 +245,29 @@ def qlora_adamw_step(param: torch.Tensor, grad: torch.Tensor, m: torch.Tensor, v
                                   _stream(stream)), "qlora_adamw_step")
 
 
+def _page_args(dev: torch.Tensor, host: torch.Tensor):
+    if not dev.is_cuda or host.is_cuda or not host.is_pinned():
+        raise QLoRAError("paging copies between a device tensor and a pinned host tensor")
+    if not dev.is_contiguous() or not host.is_contiguous() or dev.nbytes != host.nbytes:
+        raise QLoRAError("paging needs two contiguous tensors of the same size")
+
+
+def qlora_state_page_out(dev: torch.Tensor, host: torch.Tensor, stream=None) -> torch.Tensor:
+    """Copy optimizer state from device memory into a pinned host tensor (asynchronous on the
+    stream).  Returns `host`."""
+    _page_args(dev, host)
+    _check(lib().qlora_state_page_out(_ptr(dev), _ptr(host), dev.nbytes, _stream(stream)), "qlora_state_page_out")
+    return host
+
+
+def qlora_state_page_in(host: torch.Tensor, dev: torch.Tensor, stream=None) -> torch.Tensor:
+    """Copy optimizer state from a pinned host tensor back into device memory (asynchronous
+    on the stream).  Returns `dev`."""
+    _page_args(dev, host)
+    _check(lib().qlora_state_page_in(_ptr(host), _ptr(dev), dev.nbytes, _stream(stream)), "qlora_state_page_in")
+    return dev
+
+
 def qlora_profile_enable(enable: bool = True):
     _check(lib().qlora_profile_enable(int(enable)), "qlora_profile_enable")
 

@@ -65,6 +65,8 @@ SIGNATURES = {
     "qlora_linear_bwd": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64, C.POINTER(qlora_nf4), C.c_void_p,
                                    C.c_void_p, C.c_int32, C.c_float, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                    C.c_size_t, C.c_void_p]),
+    "qlora_state_page_out": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "qlora_state_page_in": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     "qlora_profile_enable": (C.c_int, [C.c_int32]),
     "qlora_profile_read": (C.c_int32, [C.POINTER(qlora_kernel_time), C.c_int32, C.c_int32]),
 }

@@ -541,6 +541,48 @@ qlora_status qlora_merge_adapter(const qlora_nf4* w, const uint16_t* A, const ui
   return QLORA_OK;
 }
 
+}  // extern "C"
+
+namespace {
+// hipMemoryTypeHost for pinned host memory, hipMemoryTypeDevice for device memory; -1 when the
+// runtime does not know the pointer (pageable host memory)
+int memory_type(const void* p) {
+  hipPointerAttribute_t a;
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();   // clear the sticky error the query leaves for unknown pointers
+    return -1;
+  }
+  return (int)a.type;
+}
+
+qlora_status page_copy(const void* src, void* dst, size_t bytes, bool to_host, hipStream_t stream) {
+  if (!src || !dst) return QLORA_ERR_NULL;
+  if (bytes % 4 != 0) return QLORA_ERR_SHAPE;
+  if (!aligned16(src) || !aligned16(dst)) return QLORA_ERR_ALIGN;
+  if (bytes == 0) return QLORA_OK;
+  const char* s = static_cast<const char*>(src);
+  const char* d = static_cast<const char*>(dst);
+  if (s < d + bytes && d < s + bytes) return QLORA_ERR_SHAPE;
+  const void* host = to_host ? dst : src;
+  const void* dev = to_host ? src : dst;
+  if (memory_type(host) != (int)hipMemoryTypeHost || memory_type(dev) != (int)hipMemoryTypeDevice)
+    return QLORA_ERR_UNSUPPORTED;
+  ProfScope ps(to_host ? "page_out_copy" : "page_in_copy", stream);
+  QL_HIP(hipMemcpyAsync(dst, src, bytes, to_host ? hipMemcpyDeviceToHost : hipMemcpyHostToDevice, stream));
+  return QLORA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+qlora_status qlora_state_page_out(const void* device, void* host, size_t bytes, hipStream_t stream) {
+  return page_copy(device, host, bytes, true, stream);
+}
+
+qlora_status qlora_state_page_in(const void* host, void* device, size_t bytes, hipStream_t stream) {
+  return page_copy(host, device, bytes, false, stream);
+}
+
 qlora_status qlora_adamw_step(float* param, uint16_t* param_bf16, const float* grad, float* m, float* v, int64_t n,
                               int64_t step, float lr, float beta1, float beta2, float eps, float weight_decay,
                               hipStream_t stream) {

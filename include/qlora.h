@@ -226,6 +226,22 @@ qlora_status qlora_adamw_step(float* param, uint16_t* param_bf16, const float* g
                               int64_t step, float lr, float beta1, float beta2, float eps, float weight_decay,
                               hipStream_t stream);
 
+/* Paging of optimizer state ("QLoRA: Efficient Finetuning of Quantized LLMs", section
+ * "Paged optimizers": the adapters' optimizer state is moved out to CPU memory when GPU
+ * memory runs short and brought back before the optimizer step needs it).  The state stays
+ * in device memory by default; these calls move `bytes` bytes of it between device memory
+ * and pinned host memory with the GPU's copy engines, asynchronously on `stream` (the copy
+ * is ordered after earlier work on the stream and before later work, so a page-in followed
+ * by qlora_adamw_step on the same stream updates the paged-in state).
+ *   qlora_state_page_out: device -> host;  qlora_state_page_in: host -> device.
+ * Requires: both pointers non-NULL and 16-byte aligned; bytes a multiple of 4 (0 is a
+ * no-op); `host` inside pinned host memory (hipHostMalloc, torch pin_memory) and `device`
+ * inside device memory, as the HIP runtime reports them (UNSUPPORTED otherwise: pageable
+ * memory would make the copy synchronous); the two ranges must not overlap.  The caller
+ * keeps the host buffer alive until the copy has completed.                            */
+qlora_status qlora_state_page_out(const void* device, void* host, size_t bytes, hipStream_t stream);
+qlora_status qlora_state_page_in(const void* host, void* device, size_t bytes, hipStream_t stream);
+
 /* Optional per-kernel timing, for benchmarking.  While enabled, every kernel
  * launch of this library is bracketed by HIP events on its stream.
  * qlora_profile_read synchronizes those events and returns, per kernel name,

@@ -191,6 +191,20 @@ def test_adamw_validation(lib):
     assert f(ok, C.c_void_p(0x100002), ok, ok, ok, 8, 1, 1e-3, 0.9, 0.999, 1e-8, 0.0, None) == 3
 
 
+def test_page_validation(lib):
+    """Argument checks of the paging calls that need no device: NULL, size, alignment,
+    overlap, and the no-op of zero bytes."""
+    a, b = C.c_void_p(0x100000), C.c_void_p(0x200000)
+    for f in (lib.qlora_state_page_out, lib.qlora_state_page_in):
+        assert f(a, b, 0, None) == 0                            # nothing to copy
+        assert f(None, b, 64, None) == 1
+        assert f(a, None, 64, None) == 1
+        assert f(a, b, 6, None) == 2                            # not whole floats
+        assert f(C.c_void_p(0x100008), b, 64, None) == 3
+        assert f(a, C.c_void_p(0x200004), 64, None) == 3
+        assert f(a, C.c_void_p(0x100010), 64, None) == 2        # overlapping ranges
+
+
 def test_status_strings(lib):
     for s in range(7):
         assert lib.qlora_status_str(s)

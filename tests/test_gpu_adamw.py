@@ -97,3 +97,52 @@ def test_adamw_state_in_host_memory():
         assert torch.equal(a, b.cpu())
     assert torch.equal(hb, db)
 
+
+
+def test_state_paged_out_and_back_in():
+    """The optimizer state stays in device memory; between steps it is paged out to pinned
+    host memory, the device copies are overwritten (the memory taken by something else),
+    and it is paged back in ("Paged optimizers").  Every later step gives the same bits as
+    a run whose state never left the device, and the parameters stay within the oracle's
+    bound."""
+    require_gpu()
+    n = 4096 * 64 + 7
+    rng = np.random.default_rng(23)
+    p0 = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    dev = torch.device("cuda", 0)
+    lr, b1, b2, eps, wd = (float(np.float32(x)) for x in (2e-4, 0.9, 0.999, 1e-8, 0.01))
+    state = {k: torch.from_numpy(p0.copy()).to(dev) if k == "p" else torch.zeros(n, device=dev) for k in "pmv"}
+    ref = {k: v.clone() for k, v in state.items()}
+    pinned = {k: torch.empty(n, dtype=torch.float32).pin_memory() for k in "pmv"}
+    rp, rm, rv = p0.astype(np.float64), np.zeros(n), np.zeros(n)
+    for t in range(1, 7):
+        g = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+        gd = torch.from_numpy(g).to(dev)
+        if t in (3, 5):
+            log("page out / scribble / page in before step", t)
+            for k in "pmv":
+                Q.qlora_state_page_out(state[k], pinned[k])
+            for k in "pmv":
+                state[k].fill_(float("nan"))        # the device memory is reused meanwhile
+            for k in "pmv":
+                Q.qlora_state_page_in(pinned[k], state[k])
+        Q.qlora_adamw_step(state["p"], gd, state["m"], state["v"], t, lr, b1, b2, eps, wd)
+        Q.qlora_adamw_step(ref["p"], gd, ref["m"], ref["v"], t, lr, b1, b2, eps, wd)
+        rp, rm, rv = adamw.adamw_step(rp, g, rm, rv, t, lr, b1, b2, eps, wd)
+    torch.cuda.synchronize()
+    for k in "pmv":
+        assert torch.equal(state[k], ref[k]), k
+    gp = host(state["p"]).astype(np.float64)
+    assert np.max(np.abs(gp - rp)) <= 8 * 2.0 ** -24 * (np.max(np.abs(rp)) + 7 * lr)
+
+
+def test_page_calls_refuse_pageable_host_memory():
+    require_gpu()
+    d = torch.zeros(1024, device="cuda")
+    h = torch.zeros(1024)                         # pageable: not pinned
+    lib = Q.lib()
+    import ctypes
+    st = lib.qlora_state_page_out(ctypes.c_void_p(d.data_ptr()), ctypes.c_void_p(h.data_ptr()), 4096, None)
+    assert st == 4                                # QLORA_ERR_UNSUPPORTED
+    st = lib.qlora_state_page_in(ctypes.c_void_p(h.data_ptr()), ctypes.c_void_p(d.data_ptr()), 4096, None)
+    assert st == 4
