@@ -219,8 +219,8 @@ FwdWs fwd_layout(void* base, int64_t M, int64_t in, int64_t out, int32_t r) {
   const int64_t Mm = std::max<int64_t>(M, 1);
   FwdWs ws;
   ws.t = lora_problem(gemm_T(nullptr, nullptr, Mm, in, r), epi_none(), kMaxSplits);
-  ws.gv = gemv_plan(Mm, in, out, rp);
   const int64_t st = split_stages(M, in, out);
+  ws.gv = gemv_plan(Mm, in, out, rp, st != 0);
   if (st) {   // the split forward's slices take the place of the weight slices
     ws.gv.splits = (int)split_count(in, st);
     ws.gv.tpart = (size_t)ws.gv.splits * Mm * ws.gv.npad;

@@ -47,7 +47,7 @@ constexpr int RGR = 16;           // rows per row group
 constexpr int GROWS = 64;         // adapter columns per adapter workgroup
 constexpr int ACH = 64;           // rows of A per LDS chunk (8 KiB)
 constexpr int XAS = 72;           // X chunk row stride in the adapter workgroups (64 + 8 padding)
-constexpr int KA = 2048;          // rows of A per adapter slice
+constexpr int KA = 2048;          // rows of A per adapter slice beside the weight pass
 constexpr int kSlotsPerCU = 2;    // resident workgroups per CU the grid is sized for (TG = 1)
 constexpr int RG_ROUND = 4;       // row groups x token groups per round (one LDS hand-over each)
 
@@ -72,6 +72,7 @@ struct GemvParams {
   int64_t rranges;      // weight workgroups per slice (contiguous ranges of row groups)
   int64_t agroups;      // adapter workgroups per adapter slice
   int asplits;
+  int ka;               // rows of A per adapter slice (a multiple of 64)
   int ngr;              // 16-token groups
   NF4Table tab;
 };
@@ -300,7 +301,7 @@ __device__ __forceinline__ void weight_group(const GemvParams& p, int bid, uint8
   }
 }
 
-// ---- adapter workgroup: columns j0.. of A over a slice of KA rows; A is [K][r], columns
+// ---- adapter workgroup: columns j0.. of A over a slice of ka rows; A is [K][r], columns
 // past r read zero.  Loads run in groups of 4 chunks (of 64 rows), one group ahead; each
 // chunk of A and of X is stored to LDS (two buffers) and taken by waves 0..3 (first 32 rows)
 // and 4..7 (the rest).
@@ -314,9 +315,9 @@ __device__ __forceinline__ void adapter_group(const GemvParams& p, int bid, uint
   const int grp = rest / nsp;
   const int split = rest - grp * nsp;
   const int m0 = tgi * 16;
-  const int kb_beg = split * (KA / 64);
+  const int kb_beg = split * (p.ka / 64);
   const int nkb = (int)(p.K / 64);
-  const int nkb_s = min(nkb, kb_beg + KA / 64) - kb_beg;      // blocks (64-row chunks) in this slice
+  const int nkb_s = min(nkb, kb_beg + p.ka / 64) - kb_beg;      // blocks (64-row chunks) in this slice
   const int M = min((int)p.M - m0, 16);      // tokens of this group
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -542,7 +543,9 @@ void launch_gemv_variant(bool dq, int bm, int tg, dim3 grid, size_t lds, const G
 
 // Weight slices of SLB blocks, each split into contiguous ranges of 16-row groups, and
 // adapter slices of KA rows of A.  The grid fills kSlotsPerCU workgroups per CU in one round.
-GemvPlan gemv_plan(int64_t M, int64_t K, int64_t N, int64_t rp) {
+// adapters_only (a launch of X A alone): slices of at least 256 rows, as many as it takes for
+// the adapter workgroups to reach about one per CU.
+GemvPlan gemv_plan(int64_t M, int64_t K, int64_t N, int64_t rp, bool adapters_only) {
   const int64_t nkb = K / 64;
   const int64_t Mm = std::max<int64_t>(M, 1);
   GemvPlan pl;
@@ -553,7 +556,13 @@ GemvPlan gemv_plan(int64_t M, int64_t K, int64_t N, int64_t rp) {
   pl.rgroups = (N + RGR - 1) / RGR;
   pl.npad = pl.rgroups * RGR;
   pl.agroups = rp / GROWS;
-  pl.asplits = (int)((K + KA - 1) / KA);
+  int64_t ka = KA;
+  if (adapters_only) {
+    const int64_t want = std::max<int64_t>(1, 256 / (pl.agroups * pl.ngr));
+    ka = std::max<int64_t>(256, ((K + want - 1) / want + 255) / 256 * 256);
+  }
+  pl.ka = (int)std::min<int64_t>(ka, (K + 63) / 64 * 64);
+  pl.asplits = (int)((K + pl.ka - 1) / pl.ka);
   const int64_t aw = pl.agroups * pl.asplits * pl.ngr;
   pl.rranges = std::max<int64_t>(1, std::min<int64_t>(pl.rgroups, (slots - aw) / pl.splits));
   pl.tpart = (size_t)pl.splits * Mm * pl.npad;
@@ -570,13 +579,14 @@ hipError_t launch_gemv(const uint16_t* X, int64_t M, int64_t K, int64_t N, const
   const uint64_t nchunk = (uint64_t)N * K / 64, nblk = ((uint64_t)N * K) >> w.bshift;
   GemvParams p{X, M, K, N, w, nchunk * kBlockBytes, w.dq ? nblk : nblk * 4, w.dq ? ((nblk + 255) / 256) * 4 : 0,
                A, r, partial, partial + pl.tpart, pl.npad, pl.agroups * GROWS, pl.splits, pl.rgroups,
-               pl.rranges, pl.agroups, pl.asplits, pl.ngr, nf4_table(w.cb)};
-  const size_t lds = std::max(kLdsWeight, kLdsAdapter);
+               pl.rranges, pl.agroups, pl.asplits, pl.ka, pl.ngr, nf4_table(w.cb)};
+  // X A alone: the TG = 1 code (the adapter workgroups do not depend on TG) and their LDS only
+  const size_t lds = adapters_only ? kLdsAdapter : std::max(kLdsWeight, kLdsAdapter);
   ProfScope ps("k_fwd_nf4_gemv", s);
   const int64_t n_adapter = pl.agroups * pl.asplits * pl.ngr;
   const dim3 grid((unsigned)((adapters_only ? 0 : pl.rranges * pl.splits) + n_adapter));
   const int bm = w.bshift == 6 ? 0 : w.bshift > 6 ? 1 : 2;
-  launch_gemv_variant<1>(w.dq != 0, bm, pl.tg, grid, lds, p, s);
+  launch_gemv_variant<1>(w.dq != 0, bm, adapters_only ? 1 : pl.tg, grid, lds, p, s);
   return hipGetLastError();
 }
 

@@ -101,12 +101,13 @@ struct GemvPlan {
   int64_t rranges;            // weight workgroups per slice (contiguous ranges of row groups)
   int64_t npad;               // weight partial row length (rgroups * 16)
   int64_t agroups;            // 64-column adapter groups
-  int asplits;                // adapter slices of 2048 rows of A
+  int asplits;                // adapter slices of ka rows of A
+  int ka;
   int ngr;                    // 16-token groups of the batch (ceil(M / 16))
   int tg;                     // token groups each weight lane feeds (1, 2 or 4 >= ngr)
   size_t tpart;               // float offset of the adapter partials
 };
-GemvPlan gemv_plan(int64_t M, int64_t K, int64_t N, int64_t rp);
+GemvPlan gemv_plan(int64_t M, int64_t K, int64_t N, int64_t rp, bool adapters_only = false);
 size_t gemv_partial_floats(const GemvPlan& pl, int64_t M);
 // adapters_only: launch only the X A workgroups (their partials feed the epilogue after the
 // split large-M forward)
