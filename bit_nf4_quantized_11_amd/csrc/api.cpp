@@ -375,8 +375,7 @@ qlora_status qlora_quantize_nf4(const uint16_t* W, int64_t rows, int64_t cols, c
     const QuantWs q = quant_layout(ws, numel, block);
     QL_HIP(launch_fill_u32(reinterpret_cast<uint32_t*>(q.hist), 512 * kHistCopies, 0u, stream));
     QL_HIP(launch_quantize(W, numel, out->codebook, block, out->codes, q.absmax, q.hist, stream));
-    QL_HIP(launch_dq_mean(q.hist, nblk, out->mu, stream));
-    QL_HIP(launch_dq_encode(q.absmax, nblk, out->mu, static_cast<uint8_t*>(out->absmax), out->c1, stream));
+    QL_HIP(launch_dq_encode(q.absmax, nblk, q.hist, out->mu, static_cast<uint8_t*>(out->absmax), out->c1, stream));
   } else {
     QL_HIP(launch_quantize(W, numel, out->codebook, block, out->codes, static_cast<float*>(out->absmax), nullptr,
                            stream));

@@ -18,7 +18,10 @@
 // Built with -ffp-contract=off so no multiply-add is fused.
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
+
+#include "common.h"
 
 namespace qlora {
 
@@ -117,6 +120,57 @@ static const Codebook& codebook(int which) {
 const float* codebook_levels_host(int which) { return codebook(which).level; }
 
 const float* codebook_thresholds_host(int which) { return codebook(which).thr; }
+
+// Order-preserving map between fp32 values and 32-bit keys (-0 and +0 adjacent).
+static uint32_t okey(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+static float ofloat(uint32_t k) {
+  const uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
+// For every bin b: lo = the smallest fp32 value whose bin is b (lut_bin is non-decreasing),
+// hi = the largest.  A threshold below lo is below every value of the bin, one at or above
+// hi is above or equal to every value of it; at most one threshold may lie in [lo, hi).
+static ThrLut make_lut(const float* thr) {
+  ThrLut L;
+  const uint32_t kmin = okey(-INFINITY), kmax = okey(INFINITY);
+  uint32_t first[kLutBins + 1];   // first key whose bin is >= b
+  for (int b = 0; b <= kLutBins; ++b) {
+    if (b == 0) { first[b] = kmin; continue; }
+    if (b == kLutBins) { first[b] = kmax + 1u; continue; }
+    uint32_t lo = kmin, hi = kmax;   // lut_bin(ofloat(hi)) >= b > lut_bin(ofloat(kmin)) = 0
+    while (lo + 1u < hi) {
+      const uint32_t mid = lo + (hi - lo) / 2u;
+      if (lut_bin(ofloat(mid)) >= b) hi = mid; else lo = mid;
+    }
+    first[b] = hi;
+  }
+  for (int b = 0; b < kLutBins; ++b) {
+    const uint32_t klo = first[b], khi = first[b + 1] - 1u;   // keys of the bin's values
+    int below = 0, inside = 0;
+    float t = INFINITY;
+    for (int k = 0; k < 15; ++k) {
+      const uint32_t kt = okey(thr[k]);
+      if (kt < klo) ++below;
+      else if (kt < khi) { ++inside; t = thr[k]; }
+    }
+    if (inside > 1) std::abort();   // never for the three tables: thresholds are >= 0.08 apart
+    L.t[b] = t;
+    L.base[b] = (uint32_t)below;
+  }
+  return L;
+}
+
+const ThrLut& thr_lut_host(int which) {
+  static const ThrLut luts[3] = {make_lut(codebook(0).thr), make_lut(codebook(1).thr), make_lut(codebook(2).thr)};
+  return luts[which];
+}
 
 const float* nf4_levels_host() { return codebook(0).level; }
 

@@ -18,7 +18,7 @@ namespace qlora {
 constexpr int kBlock = 64;    // weights per NF4 block
 constexpr int kSuper = 256;   // block constants per second-level group
 constexpr int kBlockBytes = 32;   // code bytes per 64 weights (the code layout's chunk)
-constexpr int kHistCopies = 64;   // copies of the 256-bin exponent histogram (quantize workspace)
+constexpr int kHistCopies = 16;   // copies of the 256-bin exponent histogram (quantize workspace)
 
 // Passed by value to every kernel that encodes or decodes NF4 (lives in SGPRs /
 // the kernel-argument segment).
@@ -27,6 +27,26 @@ struct NF4Table {
   float thr[15];
   float pad_;
 };
+
+// Encoder table: the normalized weights' range split into kLutBins bins (bin_of below); for
+// each bin, the number of thresholds that lie below every value the bin can hold, and the one
+// threshold (or +inf) that lies inside it.  The code of x is base[b] + (x > t[b]), which equals
+// the number of thresholds below x exactly, for every fp32 x (thresholds are at least two bins
+// apart in every table).
+constexpr int kLutBins = 64;
+struct ThrLut {
+  float t[kLutBins];
+  uint32_t base[kLutBins];
+};
+
+// The bin of a normalized weight: floor(32 x + 32) computed with one fused multiply-add,
+// clamped to [0, 63] (NaN -> 0).  Host and device evaluate the same IEEE operations.
+__host__ __device__ __forceinline__ int lut_bin(float x) {
+  float y = __builtin_fmaf(x, 32.0f, 32.0f);
+  y = __builtin_fmaxf(y, 0.0f);
+  y = __builtin_fminf(y, (float)(kLutBins - 1));
+  return (int)__builtin_floorf(y);
+}
 
 // Describes a quantized weight inside kernels.
 struct NF4View {

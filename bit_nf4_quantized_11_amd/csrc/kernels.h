@@ -18,6 +18,8 @@ constexpr int kNumCodebooks = 3;   // NF4, FP4, INT4
 const float* codebook_levels_host(int which);
 const float* codebook_thresholds_host(int which);
 NF4Table nf4_table(int which);
+// The encoder's bin table of a codebook (computed once per codebook, see codebook.cpp).
+const ThrLut& thr_lut_host(int which);
 
 // Argument checks of qlora_linear_fwd other than the workspace (api.cpp).
 qlora_status linear_fwd_check(const uint16_t* X, int64_t M, const qlora_nf4* w, const uint16_t* A, const uint16_t* B,
@@ -35,9 +37,10 @@ struct ProfScope {
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
 hipError_t launch_quantize(const uint16_t* W, int64_t numel, int codebook, int block, uint8_t* codes,
                            float* absmax_f32, unsigned long long* hist, hipStream_t s);
-hipError_t launch_dq_mean(const unsigned long long* hist, int64_t nblk, float* mu, hipStream_t s);
-hipError_t launch_dq_encode(const float* absmax_f32, int64_t nblk, const float* mu, uint8_t* c2, float* c1,
-                            hipStream_t s);
+// mu from the exponent histogram (every workgroup forms it; the first stores it), then c1 and
+// the E4M3 codes of every group of 256 block constants
+hipError_t launch_dq_encode(const float* absmax_f32, int64_t nblk, const unsigned long long* hist, float* mu,
+                            uint8_t* c2, float* c1, hipStream_t s);
 hipError_t launch_dequant(const NF4View& w, int64_t numel, uint16_t* out, hipStream_t s);
 
 // ---- small rank-r products (lora.hip) ----------------------------------------------------

@@ -18,33 +18,11 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// The 15 thresholds held in VGPRs (loaded once per thread): a data-dependent index into the
-// kernel-argument table would become a dependent memory load per search level.
-struct Thr {
-  float v[15];
-};
-
-__device__ __forceinline__ Thr thr_regs(const NF4Table& t) {
-  Thr h;
-#pragma unroll
-  for (int k = 0; k < 15; ++k) {
-    h.v[k] = t.thr[k];
-    asm volatile("" : "+v"(h.v[k]));
-  }
-  return h;
-}
-
-__device__ __forceinline__ uint32_t nf4_encode(float x, const Thr& t) {
-  // code = #{k : x > thr[k]} by a 4-level binary search over the sorted thresholds
-  const bool b3 = x > t.v[7];
-  const bool b2 = x > (b3 ? t.v[11] : t.v[3]);
-  const float t1a = b2 ? t.v[13] : t.v[9], t1b = b2 ? t.v[5] : t.v[1];
-  const bool b1 = x > (b3 ? t1a : t1b);
-  const float q3 = b1 ? t.v[14] : t.v[12], q2 = b1 ? t.v[10] : t.v[8];
-  const float q1 = b1 ? t.v[6] : t.v[4], q0 = b1 ? t.v[2] : t.v[0];
-  const float t0 = b3 ? (b2 ? q3 : q2) : (b2 ? q1 : q0);
-  const bool b0 = x > t0;
-  return ((uint32_t)b3 << 3) | ((uint32_t)b2 << 2) | ((uint32_t)b1 << 1) | (uint32_t)b0;
+// Code of a normalized weight: the number of thresholds below x, read off the encoder's bin
+// table (see ThrLut in common.h) held in LDS as {threshold, base} pairs.
+__device__ __forceinline__ uint32_t lut_encode(float x, const float2* __restrict__ lut) {
+  const float2 e = lut[lut_bin(x)];
+  return __float_as_uint(e.y) + (x > e.x ? 1u : 0u);
 }
 
 // L = block / 8 lanes per block, eight consecutive weights per lane (one 16-byte load, one
@@ -57,13 +35,14 @@ template <int L>
 __global__ __launch_bounds__(kThreads) void k_nf4_quantize(const uint16_t* __restrict__ W, int64_t numel,
                                                            int64_t ncode_blk, uint8_t* __restrict__ codes,
                                                            float* __restrict__ absmax,
-                                                           unsigned long long* __restrict__ hist, NF4Table tab) {
+                                                           unsigned long long* __restrict__ hist, ThrLut lut) {
   __shared__ unsigned long long lhist[256];
+  __shared__ float2 slut[kLutBins];
   const bool dq = hist != nullptr;
   if (dq) lhist[threadIdx.x] = 0ull;
+  if (threadIdx.x < kLutBins) slut[threadIdx.x] = make_float2(lut.t[threadIdx.x], __uint_as_float(lut.base[threadIdx.x]));
   __syncthreads();
   const int sub = threadIdx.x & (L - 1);
-  const Thr thr = thr_regs(tab);
   const int64_t nblk = (numel + 8 * L - 1) / (8 * L);
   const int64_t stride = (int64_t)gridDim.x * (kThreads / L);
   for (int64_t blk = (int64_t)blockIdx.x * (kThreads / L) + (threadIdx.x / L); blk < ncode_blk; blk += stride) {
@@ -89,7 +68,7 @@ __global__ __launch_bounds__(kThreads) void k_nf4_quantize(const uint16_t* __res
     const float inv = m ? (float)(1.0 / (double)a) : 0.0f;
     uint32_t c[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = nf4_encode(__fmul_rn(bf16_to_f32(h[i]), inv), thr);
+    for (int i = 0; i < 8; ++i) c[i] = lut_encode(__fmul_rn(bf16_to_f32(h[i]), inv), slut);
     uint32_t packed = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) packed |= (c[i] | (c[i + 4] << 4)) << (8 * i);
@@ -111,11 +90,12 @@ __global__ __launch_bounds__(kThreads) void k_nf4_quantize(const uint16_t* __res
 // mu = fl32(S / nblk), S = the exact sum of all block constants rounded once to float64.
 // hist[E] = sum of the 8-bit significands (implicit bit included) of the constants whose
 // bf16 exponent field is E, so S = sum_E hist[E] * 2^(E - 134).  The exact integer
-// sum_E hist[E] << E is built in 64-bit words, then rounded to nearest even.
-__global__ __launch_bounds__(256) void k_dq_mean(const unsigned long long* __restrict__ hist, int64_t nblk,
-                                                 float* __restrict__ mu) {
+// sum_E hist[E] << E is built in 64-bit words, then rounded to nearest even.  Called by all
+// kThreads threads of a workgroup; every thread gets mu.
+__device__ float exact_mean(const unsigned long long* __restrict__ hist, int64_t nblk) {
   __shared__ unsigned long long tot[256];
   __shared__ unsigned long long nonzero[4];
+  __shared__ float mu_s;
   {
     unsigned long long v = 0;
 #pragma unroll 16
@@ -125,85 +105,95 @@ __global__ __launch_bounds__(256) void k_dq_mean(const unsigned long long* __res
     if ((threadIdx.x & 63) == 0) nonzero[threadIdx.x >> 6] = b;
   }
   __syncthreads();
-  if (threadIdx.x != 0) return;
-  constexpr int NW = 7;   // 448 bits: 2^254 * 2^64 fits
-  unsigned long long acc[NW];
+  if (threadIdx.x == 0) {
+    constexpr int NW = 7;   // 448 bits: 2^254 * 2^64 fits
+    unsigned long long acc[NW];
 #pragma unroll
-  for (int k = 0; k < NW; ++k) acc[k] = 0ull;
-  // only the occupied exponent bins, in increasing order (bin 0 only ever holds zeros)
-  for (int wv = 0; wv < 4; ++wv)
-  for (unsigned long long bits = nonzero[wv]; bits; bits &= bits - 1ull) {
-    const int E = wv * 64 + __builtin_ctzll(bits);
-    if (E == 0 || E == 255) continue;
-    const unsigned long long v = tot[E];
-    const int w = E >> 6, sh = E & 63;
-    const unsigned long long lo = v << sh;
-    const unsigned long long hi = sh ? (v >> (64 - sh)) : 0ull;
-    unsigned long long s = acc[w] + lo;
-    unsigned long long carry = s < lo;
-    acc[w] = s;
-    s = acc[w + 1] + hi;
-    unsigned long long c2 = s < hi;
-    s += carry;
-    c2 += (s < carry);
-    acc[w + 1] = s;
-    for (int k = w + 2; c2 && k < NW; ++k) {
-      acc[k] += 1ull;
-      c2 = (acc[k] == 0ull);
+    for (int k = 0; k < NW; ++k) acc[k] = 0ull;
+    // only the occupied exponent bins, in increasing order (bin 0 only ever holds zeros)
+    for (int wv = 0; wv < 4; ++wv)
+    for (unsigned long long bits = nonzero[wv]; bits; bits &= bits - 1ull) {
+      const int E = wv * 64 + __builtin_ctzll(bits);
+      if (E == 0 || E == 255) continue;
+      const unsigned long long v = tot[E];
+      const int w = E >> 6, sh = E & 63;
+      const unsigned long long lo = v << sh;
+      const unsigned long long hi = sh ? (v >> (64 - sh)) : 0ull;
+      unsigned long long s = acc[w] + lo;
+      unsigned long long carry = s < lo;
+      acc[w] = s;
+      s = acc[w + 1] + hi;
+      unsigned long long c2 = s < hi;
+      s += carry;
+      c2 += (s < carry);
+      acc[w + 1] = s;
+      for (int k = w + 2; c2 && k < NW; ++k) {
+        acc[k] += 1ull;
+        c2 = (acc[k] == 0ull);
+      }
     }
+    int top = -1;
+    for (int k = NW - 1; k >= 0; --k)
+      if (acc[k]) { top = k * 64 + 63 - __builtin_clzll(acc[k]); break; }
+    double S = 0.0;
+    if (top >= 0 && top <= 52) {
+      S = __builtin_ldexp((double)acc[0], -134);
+    } else if (top > 52) {
+      const int low = top - 52;                      // lowest kept bit
+      auto word_at = [&](int pos) -> unsigned long long {   // 64 bits starting at bit pos
+        const int w = pos >> 6, off = pos & 63;
+        unsigned long long v = acc[w] >> off;
+        if (off && w + 1 < NW) v |= acc[w + 1] << (64 - off);
+        return v;
+      };
+      unsigned long long mant = word_at(low) & ((1ull << 53) - 1ull);
+      const int rpos = low - 1;
+      const unsigned long long round = (acc[rpos >> 6] >> (rpos & 63)) & 1ull;
+      unsigned long long sticky = 0;
+      for (int k = 0; k < (rpos >> 6); ++k) sticky |= acc[k];
+      if (rpos & 63) sticky |= acc[rpos >> 6] & ((1ull << (rpos & 63)) - 1ull);
+      if (round && (sticky || (mant & 1ull))) mant += 1ull;
+      S = __builtin_ldexp((double)mant, low - 134);
+    }
+    mu_s = (float)(S / (double)nblk);
   }
-  int top = -1;
-  for (int k = NW - 1; k >= 0; --k)
-    if (acc[k]) { top = k * 64 + 63 - __builtin_clzll(acc[k]); break; }
-  double S = 0.0;
-  if (top >= 0 && top <= 52) {
-    S = __builtin_ldexp((double)acc[0], -134);
-  } else if (top > 52) {
-    const int low = top - 52;                      // lowest kept bit
-    auto word_at = [&](int pos) -> unsigned long long {   // 64 bits starting at bit pos
-      const int w = pos >> 6, off = pos & 63;
-      unsigned long long v = acc[w] >> off;
-      if (off && w + 1 < NW) v |= acc[w + 1] << (64 - off);
-      return v;
-    };
-    unsigned long long mant = word_at(low) & ((1ull << 53) - 1ull);
-    const int rpos = low - 1;
-    const unsigned long long round = (acc[rpos >> 6] >> (rpos & 63)) & 1ull;
-    unsigned long long sticky = 0;
-    for (int k = 0; k < (rpos >> 6); ++k) sticky |= acc[k];
-    if (rpos & 63) sticky |= acc[rpos >> 6] & ((1ull << (rpos & 63)) - 1ull);
-    if (round && (sticky || (mant & 1ull))) mant += 1ull;
-    S = __builtin_ldexp((double)mant, low - 134);
-  }
-  *mu = (float)(S / (double)nblk);
+  __syncthreads();
+  return mu_s;
 }
 
-// One workgroup per group of 256 block constants.
+// Groups of 256 block constants, grid-stride: each workgroup first forms mu from the
+// histogram itself (the same exact sum in every workgroup, so no launch of its own), the
+// first one stores it, then every group gets c1 = max |absmax - mu| / 448 and its E4M3 codes.
 __global__ __launch_bounds__(kThreads) void k_dq_encode(const float* __restrict__ absmax, int64_t nblk,
-                                                        const float* __restrict__ mu_p, uint8_t* __restrict__ c2,
+                                                        const unsigned long long* __restrict__ hist,
+                                                        float* __restrict__ mu_out, uint8_t* __restrict__ c2,
                                                         float* __restrict__ c1_out) {
   __shared__ uint32_t wmax[kThreads / 64];
-  const int64_t j = blockIdx.x;
-  const int64_t b = j * kSuper + threadIdx.x;
-  const float mu = *mu_p;
-  const bool valid = b < nblk;
-  const float x = valid ? __fsub_rn(absmax[b], mu) : 0.0f;
-  uint32_t m = __float_as_uint(x) & 0x7FFFFFFFu;
+  const float mu = exact_mean(hist, nblk);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *mu_out = mu;
+  const int64_t nsup = (nblk + kSuper - 1) / kSuper;
+  for (int64_t j = blockIdx.x; j < nsup; j += gridDim.x) {
+    const int64_t b = j * kSuper + threadIdx.x;
+    const bool valid = b < nblk;
+    const float x = valid ? __fsub_rn(absmax[b], mu) : 0.0f;
+    uint32_t m = __float_as_uint(x) & 0x7FFFFFFFu;
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
-  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
-  __syncthreads();
-  m = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
-  float c1 = (float)((double)__uint_as_float(m) / 448.0);
-  if (c1 < 0x1p-126f) c1 = 0.0f;
-  if (threadIdx.x == 0) c1_out[j] = c1;
-  if (valid) {
-    uint32_t code = 0;
-    if (c1 != 0.0f) {
-      const float inv = (float)(1.0 / (double)c1);
-      code = e4m3_encode(__fmul_rn(x, inv));
+    for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+    __syncthreads();   // the previous group's reads of wmax are done
+    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+    __syncthreads();
+    m = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+    float c1 = (float)((double)__uint_as_float(m) / 448.0);
+    if (c1 < 0x1p-126f) c1 = 0.0f;
+    if (threadIdx.x == 0) c1_out[j] = c1;
+    if (valid) {
+      uint32_t code = 0;
+      if (c1 != 0.0f) {
+        const float inv = (float)(1.0 / (double)c1);
+        code = e4m3_encode(__fmul_rn(x, inv));
+      }
+      c2[b] = (uint8_t)code;
     }
-    c2[b] = (uint8_t)code;
   }
 }
 
@@ -272,7 +262,7 @@ hipError_t launch_quantize(const uint16_t* W, int64_t numel, int codebook, int b
   const int64_t unit = block > 64 ? block : 64;   // the code buffer holds whole blocks and 64-chunks
   const int64_t ncode_blk = (numel + unit - 1) / unit * (unit / block);
   const unsigned grid = grid_for(ncode_blk, kThreads / (block / 8), 2048);
-  const NF4Table tab = nf4_table(codebook);
+  const ThrLut& tab = thr_lut_host(codebook);
   ProfScope ps("k_nf4_quantize", s);
   if (block == 32)
     hipLaunchKernelGGL(k_nf4_quantize<4>, dim3(grid), dim3(kThreads), 0, s, W, numel, ncode_blk, codes, absmax_f32,
@@ -289,17 +279,12 @@ hipError_t launch_quantize(const uint16_t* W, int64_t numel, int codebook, int b
   return hipGetLastError();
 }
 
-hipError_t launch_dq_mean(const unsigned long long* hist, int64_t nblk, float* mu, hipStream_t s) {
-  ProfScope ps("k_dq_mean", s);
-  hipLaunchKernelGGL(k_dq_mean, dim3(1), dim3(256), 0, s, hist, nblk, mu);
-  return hipGetLastError();
-}
-
-hipError_t launch_dq_encode(const float* absmax_f32, int64_t nblk, const float* mu, uint8_t* c2, float* c1,
-                            hipStream_t s) {
+hipError_t launch_dq_encode(const float* absmax_f32, int64_t nblk, const unsigned long long* hist, float* mu,
+                            uint8_t* c2, float* c1, hipStream_t s) {
   const int64_t nsup = (nblk + kSuper - 1) / kSuper;
   ProfScope ps("k_dq_encode", s);
-  hipLaunchKernelGGL(k_dq_encode, dim3((unsigned)nsup), dim3(kThreads), 0, s, absmax_f32, nblk, mu, c2, c1);
+  hipLaunchKernelGGL(k_dq_encode, dim3(grid_for(nsup, 1, 256)), dim3(kThreads), 0, s, absmax_f32, nblk, hist, mu, c2,
+                     c1);
   return hipGetLastError();
 }
 
