@@ -88,8 +88,10 @@ def test_quantize_c3_outliers(which):
     _check(inp.W, inp.W.shape, True, f"C3-{lin.name}")
 
 
-def test_quantize_exhaustive_bf16_sweep():
-    """Every finite bf16 pattern as a weight, in blocks led by one of several absmax values."""
+@pytest.mark.parametrize("codebook", ["nf4", "fp4", "int4"])
+def test_quantize_exhaustive_bf16_sweep(codebook):
+    """Every finite bf16 pattern as a weight, in blocks led by one of several absmax values
+    (the encoder's bin table is built per codebook, so every table is swept)."""
     allb = np.arange(2 ** 16, dtype=np.uint32).astype(np.uint16)
     vals = (allb.astype(np.uint32) << 16).view(np.float32)
     finite = allb[np.isfinite(vals)]
@@ -103,8 +105,8 @@ def test_quantize_exhaustive_bf16_sweep():
         sel = np.concatenate([sel, np.zeros(pad, np.uint16)]).reshape(-1, 63)
         blocks.append(np.concatenate([np.full((sel.shape[0], 1), ab, np.uint16), sel], axis=1))
     w = np.concatenate(blocks).reshape(-1)
-    _check(w, (1, w.size), True, "sweep")
-    _check(w, (1, w.size), False, "sweep")
+    _check(w, (1, w.size), True, "sweep", codebook)
+    _check(w, (1, w.size), False, "sweep", codebook)
 
 
 def test_quantize_degenerate_blocks():
