@@ -161,38 +161,50 @@ __device__ float exact_mean(const unsigned long long* __restrict__ hist, int64_t
   return mu_s;
 }
 
-// Groups of 256 block constants, grid-stride: each workgroup first forms mu from the
-// histogram itself (the same exact sum in every workgroup, so no launch of its own), the
-// first one stores it, then every group gets c1 = max |absmax - mu| / 448 and its E4M3 codes.
+// Groups of 256 block constants, one wave per group (4 constants per lane, a wave-wide
+// max), grid-stride over the groups.  Each workgroup first forms mu from the histogram itself
+// (the same exact sum in every workgroup, so no launch of its own); the first one stores it.
+// Then c1 = max |absmax - mu| / 448 and the E4M3 codes of the group.
 __global__ __launch_bounds__(kThreads) void k_dq_encode(const float* __restrict__ absmax, int64_t nblk,
                                                         const unsigned long long* __restrict__ hist,
                                                         float* __restrict__ mu_out, uint8_t* __restrict__ c2,
                                                         float* __restrict__ c1_out) {
-  __shared__ uint32_t wmax[kThreads / 64];
+  static_assert(kSuper == 4 * 64, "a group is one wave of 4 constants per lane");
   const float mu = exact_mean(hist, nblk);
   if (blockIdx.x == 0 && threadIdx.x == 0) *mu_out = mu;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t nsup = (nblk + kSuper - 1) / kSuper;
-  for (int64_t j = blockIdx.x; j < nsup; j += gridDim.x) {
-    const int64_t b = j * kSuper + threadIdx.x;
-    const bool valid = b < nblk;
-    const float x = valid ? __fsub_rn(absmax[b], mu) : 0.0f;
-    uint32_t m = __float_as_uint(x) & 0x7FFFFFFFu;
+  for (int64_t j = (int64_t)blockIdx.x * (kThreads / 64) + wave; j < nsup; j += (int64_t)gridDim.x * (kThreads / 64)) {
+    const int64_t b0 = j * kSuper + lane * 4;
+    float x[4];
+    if (b0 + 4 <= nblk) {
+      const float4 a = *reinterpret_cast<const float4*>(absmax + b0);
+      x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = b0 + i < nblk ? absmax[b0 + i] : mu;   // past the end: x = 0
+    }
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = __fsub_rn(x[i], mu);
+      m = max(m, __float_as_uint(x[i]) & 0x7FFFFFFFu);
+    }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
-    __syncthreads();   // the previous group's reads of wmax are done
-    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
-    __syncthreads();
-    m = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
     float c1 = (float)((double)__uint_as_float(m) / 448.0);
     if (c1 < 0x1p-126f) c1 = 0.0f;
-    if (threadIdx.x == 0) c1_out[j] = c1;
-    if (valid) {
-      uint32_t code = 0;
-      if (c1 != 0.0f) {
-        const float inv = (float)(1.0 / (double)c1);
-        code = e4m3_encode(__fmul_rn(x, inv));
-      }
-      c2[b] = (uint8_t)code;
+    if (lane == 0) c1_out[j] = c1;
+    const float inv = c1 != 0.0f ? (float)(1.0 / (double)c1) : 0.0f;
+    uint32_t packed = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) packed |= (c1 != 0.0f ? e4m3_encode(__fmul_rn(x[i], inv)) : 0u) << (8 * i);
+    if (b0 + 4 <= nblk) {
+      *reinterpret_cast<uint32_t*>(c2 + b0) = packed;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (b0 + i < nblk) c2[b0 + i] = (uint8_t)(packed >> (8 * i));
     }
   }
 }
@@ -283,7 +295,7 @@ hipError_t launch_dq_encode(const float* absmax_f32, int64_t nblk, const unsigne
                             uint8_t* c2, float* c1, hipStream_t s) {
   const int64_t nsup = (nblk + kSuper - 1) / kSuper;
   ProfScope ps("k_dq_encode", s);
-  hipLaunchKernelGGL(k_dq_encode, dim3(grid_for(nsup, 1, 256)), dim3(kThreads), 0, s, absmax_f32, nblk, hist, mu, c2,
+  hipLaunchKernelGGL(k_dq_encode, dim3(grid_for(nsup, kThreads / 64, 1024)), dim3(kThreads), 0, s, absmax_f32, nblk, hist, mu, c2,
                      c1);
   return hipGetLastError();
 }
