@@ -251,8 +251,9 @@ BwdWs bwd_layout(void* base, int64_t M, int64_t in, int64_t out, int32_t r) {
   ws.db = lora_problem(gemm_dB(nullptr, r, nullptr, Mm, out, r), epi_none(), kMaxSplits);
   const int64_t dst = dx_split_stages(M, in, out);
   const size_t pdx = dst ? (size_t)dx_split_count(out, dst) * Mm * in : 0;   // split dX partials
-  const size_t pf = std::max({lora_partial_floats(ws.t), lora_partial_floats(ws.g),
-                              lora_partial_floats(ws.da) + lora_partial_floats(ws.db), pdx});
+  // the split dX partials follow G's partials, which its epilogue still reads
+  const size_t pf = std::max({lora_partial_floats(ws.t), lora_partial_floats(ws.g) + pdx,
+                              lora_partial_floats(ws.da) + lora_partial_floats(ws.db)});
   ws.Gs = c.take<uint16_t>((size_t)Mm * rp);
   ws.T = c.take<uint16_t>((size_t)Mm * r);
   ws.partial = c.take<float>(std::max<size_t>(pf, 1));
@@ -465,13 +466,20 @@ qlora_status qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, const uint1
                                 kMaxSplits);
   pg.partial = L.partial;
   QL_HIP(launch_lora(pg, nullptr, "k_lora_dyb", stream));
-  if (pg.splits > 1) QL_HIP(launch_lora_reduce(pg, nullptr, "k_lora_dyb_reduce", stream));
+  const int64_t dst = dX ? dx_split_stages(M, in, out) : 0;
+  // with the split dX and at most 64 tokens, its epilogue sums G's partials itself (and stores
+  // Gs for dA); with more tokens every one of its in/64 column blocks would repeat that sum for
+  // its token group, which costs more than the reduce launch (measured at 256 and 512 tokens)
+  const bool fold_g = dst && pg.splits > 1 && M <= 64;
+  if (pg.splits > 1 && !fold_g) QL_HIP(launch_lora_reduce(pg, nullptr, "k_lora_dyb_reduce", stream));
   if (dX) {
-    if (const int64_t dst = dx_split_stages(M, in, out)) {
-      // few tokens, few column tiles: the reduction in slices (fp32 partials), then the
-      // slices' sum plus Gs A^T in one epilogue; the partials of Gs are consumed by now
-      QL_HIP(launch_dx_gemm_split(dY, M, in, out, v, (int)dst, L.partial, stream));
-      QL_HIP(launch_dx_split_epilogue(L.partial, (int)dx_split_count(out, dst), M, in, L.Gs, rp, A, r, dX, stream));
+    if (dst) {
+      // few tokens, few column tiles: the reduction in slices (fp32 partials, after G's),
+      // then the slices' sum plus Gs A^T in one epilogue
+      float* const dxpart = L.partial + lora_partial_floats(pg);
+      const GFold gf{fold_g ? L.partial : nullptr, pg.splits, pg.tiles_j, scale, L.Gs};
+      QL_HIP(launch_dx_gemm_split(dY, M, in, out, v, (int)dst, dxpart, stream));
+      QL_HIP(launch_dx_split_epilogue(dxpart, (int)dx_split_count(out, dst), M, in, L.Gs, rp, A, r, dX, gf, stream));
     } else {
       QL_HIP(launch_dx_gemm(dY, M, in, out, v, L.Gs, rp, A, r, dX, stream));
     }

@@ -12,7 +12,8 @@
 //
 // Split mode (few tokens, few column tiles): a workgroup covers a slice of the reduction
 // stages, skips the adapter stages and writes fp32 partials; k_dx_split_epilogue sums the
-// slices in order, adds Gs A~^T and rounds once.
+// slices in order, adds Gs A~^T and rounds once.  When the rank-r kernel left G as split-K
+// partials, the epilogue also forms Gs from them (no reduce launch) and stores it for dA.
 #include "common.h"
 #include "gemm_core.h"
 #include "kernels.h"
@@ -208,7 +209,7 @@ __global__ __launch_bounds__(NT) void k_bwd_dx_nf4_gemm(DxParams p) {
 __global__ __launch_bounds__(256) void k_dx_split_epilogue(const float* __restrict__ partial, int splits, int64_t M,
                                                           int64_t K, const uint16_t* __restrict__ Gs, int64_t rp,
                                                           const uint16_t* __restrict__ A, int64_t r,
-                                                          uint16_t* __restrict__ dX) {
+                                                          uint16_t* __restrict__ dX, GFold gf) {
   __shared__ __attribute__((aligned(16))) float sG[16 * 256];
   __shared__ __attribute__((aligned(16))) uint16_t sA[256 * 64];
   const int t = threadIdx.x;
@@ -238,15 +239,38 @@ __global__ __launch_bounds__(256) void k_dx_split_epilogue(const float* __restri
     const int idx = t + 256 * u;
     av[u] = ld16(rA, idx < apieces ? abase + (uint32_t)idx * 16 : aend);
   }
-  // Gs rows of the group: Mg rp values, at most 2 pieces per thread
+  // Gs rows of the group: Mg rp values, at most 2 pieces per thread (when Gs is in memory)
   const rsrc_t rG = make_rsrc(Gs, (uint64_t)M * rp * 2);
-  const int gpieces = Mg * (int)rp / 8;
+  const int gpieces = gf.partial ? 0 : Mg * (int)rp / 8;
   const uint32_t gbase = (uint32_t)(m0 * rp * 2), gend = (uint32_t)(M * rp * 2);
   uint4 gv[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int idx = t + 256 * u;
     gv[u] = ld16(rG, idx < gpieces ? gbase + (uint32_t)idx * 16 : gend);
+  }
+  if (gf.partial) {
+    // G from the split-K partials of the rank-r kernel ([tile][split][64][64] fp32, tile =
+    // (m / 64) tiles_j + j / 64), summed in split order, scaled and rounded as the reduce
+    // kernel would; the first column block of each token group also stores Gs for dA.
+    const int ent = Mg * (int)rp;
+    for (int e = t; e < ent; e += 256) {
+      const int m = e / (int)rp, j = e - m * (int)rp;
+      const int64_t row = m0 + m;
+      const float* base = gf.partial + (((row >> 6) * gf.tiles_j + (j >> 6)) * gf.splits) * 4096 + (row & 63) * 64 + (j & 63);
+      float pv[8];
+      float sum = 0.0f;
+      for (int s0 = 0; s0 < gf.splits; s0 += 8) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) pv[u] = base[(int64_t)min(s0 + u, gf.splits - 1) * 4096];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (s0 + u < gf.splits) sum = s0 + u == 0 ? pv[u] : __fadd_rn(sum, pv[u]);
+      }
+      const uint32_t gb = j < (int)r ? f32_to_bf16_bits(__fmul_rn(gf.scale, sum)) : 0u;
+      sG[m * 256 + j] = bf16_to_f32(gb);
+      if (blockIdx.x == 0) gf.Gs_out[row * rp + j] = (uint16_t)gb;
+    }
   }
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
@@ -356,10 +380,11 @@ hipError_t launch_dx_gemm_split(const uint16_t* dY, int64_t M, int64_t K, int64_
 }
 
 hipError_t launch_dx_split_epilogue(const float* partial, int splits, int64_t M, int64_t K, const uint16_t* Gs,
-                                    int64_t rp, const uint16_t* A, int64_t r, uint16_t* dX, hipStream_t s) {
+                                    int64_t rp, const uint16_t* A, int64_t r, uint16_t* dX, const GFold& gf,
+                                    hipStream_t s) {
   ProfScope ps("k_dx_split_epilogue", s);
   const dim3 grid((unsigned)(K / 64), (unsigned)((M + 15) / 16)), block(256);
-  hipLaunchKernelGGL(k_dx_split_epilogue, grid, block, 0, s, partial, splits, M, K, Gs, rp, A, r, dX);
+  hipLaunchKernelGGL(k_dx_split_epilogue, grid, block, 0, s, partial, splits, M, K, Gs, rp, A, r, dX, gf);
   return hipGetLastError();
 }
 

@@ -128,8 +128,18 @@ hipError_t launch_dx_gemm(const uint16_t* dY, int64_t M, int64_t K, int64_t N, c
 // (no adapter term), then the epilogue sums the slices in order, adds Gs A^T, rounds once
 hipError_t launch_dx_gemm_split(const uint16_t* dY, int64_t M, int64_t K, int64_t N, const NF4View& w, int stages,
                                 float* partial, hipStream_t s);
+// G still in split-K partials of the rank-r kernel (partial == NULL: Gs is in memory already):
+// the epilogue forms Gs = bf16(scale G) itself and stores it to Gs_out [M][rp] for dA.
+struct GFold {
+  const float* partial;   // [tile][split][64][64], tile = (m / 64) tiles_j + j / 64
+  int splits;
+  int64_t tiles_j;
+  float scale;
+  uint16_t* Gs_out;
+};
 hipError_t launch_dx_split_epilogue(const float* partial, int splits, int64_t M, int64_t K, const uint16_t* Gs,
-                                    int64_t rp, const uint16_t* A, int64_t r, uint16_t* dX, hipStream_t s);
+                                    int64_t rp, const uint16_t* A, int64_t r, uint16_t* dX, const GFold& gf,
+                                    hipStream_t s);
 
 // ---- adapter merge (merge.hip): out [N][K] = bf16(deq(W) + scale (A B)^T), K % 64 == 0 -------
 hipError_t launch_merge_adapter(const NF4View& w, int64_t N, int64_t K, const uint16_t* A, const uint16_t* B, int64_t r,

@@ -150,6 +150,7 @@ SPLIT_DX = [
     # in slices of the weight's rows (fp32 partials), then slice sums + Gs A^T in one epilogue
     (1, 512, 1000, 8),         # 4 slices of 4 stages, ragged last stage (1000 = 15 x 64 + 40)
     (16, 1024, 4096, 16),      # 16 slices of 4 stages
+    (40, 1024, 2048, 72),      # 3 token groups, rank padded to 128 (2 column tiles of G), G folded into the epilogue
     (65, 4096, 4096, 64),      # 8 slices of 8 stages
     (100, 2048, 520, 8),       # 9 stages would make only 2 slices: the plain path, ragged
     (100, 1024, 720, 8),       # 8 tiles, 12 stages: exactly 3 slices of 4, ragged last stage
