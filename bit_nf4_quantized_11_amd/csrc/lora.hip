@@ -18,6 +18,8 @@
 #include "gemm_core.h"
 #include "kernels.h"
 
+#include <algorithm>
+
 namespace qlora {
 
 namespace {
@@ -201,8 +203,50 @@ __global__ __launch_bounds__(256) void k_lora_gemm(LoraProblem p0, LoraProblem p
         part[(wi * 32 + a * 16 + 4 * (lane >> 4) + v) * TJ + wj * 32 + b * 16 + (lane & 15)] = acc[a][b][v];
 }
 
+// Four consecutive outputs of one row: a single 8-byte (bf16) or 16-byte (fp32) store where
+// the destination is aligned, else element stores.
+__device__ __forceinline__ void store4_bf16(uint16_t* dst, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  if ((reinterpret_cast<uintptr_t>(dst) & 7u) == 0) {
+    *reinterpret_cast<uint2*>(dst) = make_uint2(a | (b << 16), c | (d << 16));
+  } else {
+    dst[0] = (uint16_t)a; dst[1] = (uint16_t)b; dst[2] = (uint16_t)c; dst[3] = (uint16_t)d;
+  }
+}
+
+__device__ __forceinline__ void epi_write4(const LoraEpi& ep, int64_t I, int64_t J, int64_t i, int64_t j,
+                                           const float4& v) {
+  if (i >= I) return;
+  if (j + 4 > J) {   // the rank's ragged edge (and padding columns up to ldb)
+    epi_write(ep, I, J, i, j + 0, v.x);
+    epi_write(ep, I, J, i, j + 1, v.y);
+    epi_write(ep, I, J, i, j + 2, v.z);
+    epi_write(ep, I, J, i, j + 3, v.w);
+    return;
+  }
+  auto bf = [](float sc, float x) { return f32_to_bf16_bits(__fmul_rn(sc, x)); };
+  if (ep.out_a)
+    store4_bf16(ep.out_a + i * ep.lda + j, bf(ep.scale_a, v.x), bf(ep.scale_a, v.y), bf(ep.scale_a, v.z),
+                bf(ep.scale_a, v.w));
+  if (ep.out_b)
+    store4_bf16(ep.out_b + i * ep.ldb + j, bf(ep.scale_b, v.x), bf(ep.scale_b, v.y), bf(ep.scale_b, v.z),
+                bf(ep.scale_b, v.w));
+  if (ep.out_f) {
+    float* dst = ep.out_f + i * J + j;
+    const float4 o = make_float4(__fmul_rn(ep.scale_f, v.x), __fmul_rn(ep.scale_f, v.y), __fmul_rn(ep.scale_f, v.z),
+                                 __fmul_rn(ep.scale_f, v.w));
+    if ((reinterpret_cast<uintptr_t>(dst) & 15u) == 0) {
+      *reinterpret_cast<float4*>(dst) = o;
+    } else {
+      dst[0] = o.x; dst[1] = o.y; dst[2] = o.z; dst[3] = o.w;
+    }
+  }
+}
+
 // Sum of the split partials in split order, then the outputs.  Four consecutive
-// elements of a tile row per thread.
+// elements of a tile row per thread.  S (2, 4, 8 or 16) bounds the splits of both problems:
+// every thread issues exactly S loads (indices past the last split repeat it, unused) before
+// the first add, so it waits for memory once.
+template <int S>
 __global__ __launch_bounds__(256) void k_lora_reduce(LoraProblem p0, LoraProblem p1, int nprob) {
   const int64_t per = p0.tiles_i * p0.tiles_j * (TI * TJ / 4);
   int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -214,14 +258,13 @@ __global__ __launch_bounds__(256) void k_lora_reduce(LoraProblem p0, LoraProblem
   const int e = (int)(idx - tile * (TI * TJ / 4)) * 4;
   const int64_t ti = tile / P.tiles_j, tj = tile - ti * P.tiles_j;
   const float* base = P.partial + tile * P.splits * (TI * TJ) + e;
-  // every split's value is loaded before the first add (one memory latency, not splits)
-  float4 v[kMaxLoraSplits];
+  float4 v[S];
 #pragma unroll
-  for (int sp = 0; sp < kMaxLoraSplits; ++sp)
+  for (int sp = 0; sp < S; ++sp)
     v[sp] = *reinterpret_cast<const float4*>(base + min(sp, P.splits - 1) * (TI * TJ));
   float4 sum = v[0];
 #pragma unroll
-  for (int sp = 1; sp < kMaxLoraSplits; ++sp) {
+  for (int sp = 1; sp < S; ++sp) {
     if (sp < P.splits) {
       sum.x = __fadd_rn(sum.x, v[sp].x);
       sum.y = __fadd_rn(sum.y, v[sp].y);
@@ -229,11 +272,7 @@ __global__ __launch_bounds__(256) void k_lora_reduce(LoraProblem p0, LoraProblem
       sum.w = __fadd_rn(sum.w, v[sp].w);
     }
   }
-  const int64_t i = ti * TI + e / TJ, j = tj * TJ + e % TJ;
-  epi_write(P.ep, P.g.I, P.g.J, i, j + 0, sum.x);
-  epi_write(P.ep, P.g.I, P.g.J, i, j + 1, sum.y);
-  epi_write(P.ep, P.g.I, P.g.J, i, j + 2, sum.z);
-  epi_write(P.ep, P.g.I, P.g.J, i, j + 3, sum.w);
+  epi_write4(P.ep, P.g.I, P.g.J, ti * TI + e / TJ, tj * TJ + e % TJ, sum);
 }
 
 }  // namespace
@@ -284,8 +323,13 @@ hipError_t launch_lora_reduce(const LoraProblem& p0, const LoraProblem* p1, cons
   const LoraProblem q1 = p1 ? *p1 : p0;
   const int nprob = p1 ? 2 : 1;
   const int64_t n = (p0.tiles_i * p0.tiles_j + (p1 ? p1->tiles_i * p1->tiles_j : 0)) * (TI * TJ / 4);
+  const int most = std::max(p0.splits, p1 ? p1->splits : 1);
+  const dim3 grid((unsigned)((n + 255) / 256)), block(256);
   ProfScope ps(name, s);
-  hipLaunchKernelGGL(k_lora_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p0, q1, nprob);
+  if (most <= 2) hipLaunchKernelGGL(k_lora_reduce<2>, grid, block, 0, s, p0, q1, nprob);
+  else if (most <= 4) hipLaunchKernelGGL(k_lora_reduce<4>, grid, block, 0, s, p0, q1, nprob);
+  else if (most <= 8) hipLaunchKernelGGL(k_lora_reduce<8>, grid, block, 0, s, p0, q1, nprob);
+  else hipLaunchKernelGGL(k_lora_reduce<kMaxLoraSplits>, grid, block, 0, s, p0, q1, nprob);
   return hipGetLastError();
 }
 
