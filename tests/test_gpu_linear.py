@@ -91,6 +91,8 @@ RANK_R = [
     (2049, 1024, 1032, 24),    # ragged token tile, reduction of G not a multiple of 64, rank padded
     (1024, 1024, 1024, 256),   # largest rank
     (2048, 2048, 1088, 8),     # smallest rank
+    (2100, 4096, 4104, 24),    # 8 splits of X A and dY B^T, ragged last panel, out % 64 == 8
+    (4096, 2048, 2048, 64),    # 4 splits each
 ]
 
 
