@@ -262,7 +262,7 @@ BwdWs bwd_layout(void* base, int64_t M, int64_t in, int64_t out, int32_t r) {
 }
 
 struct QuantWs {
-  unsigned long long* hist;
+  unsigned long long* sums;   // one exact partial sum of the block constants per quantize workgroup
   float* absmax;
   size_t bytes;
 };
@@ -270,7 +270,7 @@ struct QuantWs {
 QuantWs quant_layout(void* base, int64_t numel, int block) {
   Carve c(base);
   QuantWs ws;
-  ws.hist = c.take<unsigned long long>(256 * kHistCopies);
+  ws.sums = c.take<unsigned long long>((size_t)kQuantSlots * kSumLimbs);
   ws.absmax = c.take<float>((size_t)((numel + block - 1) / block));
   ws.bytes = round_up(c.off, 256);
   return ws;
@@ -374,9 +374,9 @@ qlora_status qlora_quantize_nf4(const uint16_t* W, int64_t rows, int64_t cols, c
     if (!ws || ws_bytes < need.bytes) return QLORA_ERR_WORKSPACE;
     if (!aligned16(ws)) return QLORA_ERR_ALIGN;
     const QuantWs q = quant_layout(ws, numel, block);
-    QL_HIP(launch_fill_u32(reinterpret_cast<uint32_t*>(q.hist), 512 * kHistCopies, 0u, stream));
-    QL_HIP(launch_quantize(W, numel, out->codebook, block, out->codes, q.absmax, q.hist, stream));
-    QL_HIP(launch_dq_encode(q.absmax, nblk, q.hist, out->mu, static_cast<uint8_t*>(out->absmax), out->c1, stream));
+    QL_HIP(launch_quantize(W, numel, out->codebook, block, out->codes, q.absmax, q.sums, stream));
+    QL_HIP(launch_dq_encode(q.absmax, nblk, q.sums, quantize_grid(numel, block), out->mu,
+                            static_cast<uint8_t*>(out->absmax), out->c1, stream));
   } else {
     QL_HIP(launch_quantize(W, numel, out->codebook, block, out->codes, static_cast<float*>(out->absmax), nullptr,
                            stream));

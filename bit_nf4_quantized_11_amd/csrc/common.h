@@ -18,7 +18,8 @@ namespace qlora {
 constexpr int kBlock = 64;    // weights per NF4 block
 constexpr int kSuper = 256;   // block constants per second-level group
 constexpr int kBlockBytes = 32;   // code bytes per 64 weights (the code layout's chunk)
-constexpr int kHistCopies = 16;   // copies of the 256-bin exponent histogram (quantize workspace)
+constexpr int kQuantSlots = 512;  // quantize workgroups at most: one partial sum slot each (workspace)
+constexpr int kSumLimbs = 10;     // 32-bit limbs of an exact sum of block constants (320 bits)
 
 // Passed by value to every kernel that encodes or decodes NF4 (lives in SGPRs /
 // the kernel-argument segment).

@@ -35,11 +35,14 @@ struct ProfScope {
 
 // ---- quantize / dequantize (quant.hip) --------------------------------------------------
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
+// workgroups of the quantize launch (<= kQuantSlots): the number of exact-sum slots it writes
+int quantize_grid(int64_t numel, int block);
+// sums: kSumLimbs x quantize_grid() 64-bit words (double quantization), or NULL
 hipError_t launch_quantize(const uint16_t* W, int64_t numel, int codebook, int block, uint8_t* codes,
-                           float* absmax_f32, unsigned long long* hist, hipStream_t s);
-// mu from the exponent histogram (every workgroup forms it; the first stores it), then c1 and
-// the E4M3 codes of every group of 256 block constants
-hipError_t launch_dq_encode(const float* absmax_f32, int64_t nblk, const unsigned long long* hist, float* mu,
+                           float* absmax_f32, unsigned long long* sums, hipStream_t s);
+// mu from the quantize workgroups' exact sums (every workgroup forms it; the first stores it),
+// then c1 and the E4M3 codes of every group of 256 block constants
+hipError_t launch_dq_encode(const float* absmax_f32, int64_t nblk, const unsigned long long* sums, int nslots, float* mu,
                             uint8_t* c2, float* c1, hipStream_t s);
 hipError_t launch_dequant(const NF4View& w, int64_t numel, uint16_t* out, hipStream_t s);
 

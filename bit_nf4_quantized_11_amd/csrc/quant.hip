@@ -17,6 +17,7 @@ namespace qlora {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kQuantThreads = 1024;   // quantize workgroups: at most kQuantSlots of them
 
 // Code of a normalized weight: the number of thresholds below x, read off the encoder's bin
 // table (see ThrLut in common.h) held in LDS as {threshold, base} pairs.
@@ -27,25 +28,30 @@ __device__ __forceinline__ uint32_t lut_encode(float x, const float2* __restrict
 
 // L = block / 8 lanes per block, eight consecutive weights per lane (one 16-byte load, one
 // code dword).  Lane 0 of each group writes the fp32 block constant and, for double
-// quantization, adds it to a per-exponent histogram from which the exact sum of all
-// constants is rebuilt (integer adds: order-independent, hence deterministic).  Blocks
-// from nblk up to ncode_blk (the code buffer's padding to whole 64-element chunks) get
-// zero codes and no constant.
+// quantization, adds its significand to a per-exponent histogram in LDS.  At the end the
+// workgroup turns that histogram into the exact integer sum_E hist[E] << E (the sum of its
+// constants times 2^134, see exact_mean) and writes it to its own slot of `sums` as kSumLimbs
+// 64-bit words, word k holding the part of weight 2^(32 k) (each below 2^39, not carried):
+// integer adds only, so the result does not depend on the order, and no slot needs clearing
+// beforehand.  Blocks from nblk up to ncode_blk (the code buffer's padding to
+// whole 64-element chunks) get zero codes and no constant.
 template <int L>
-__global__ __launch_bounds__(kThreads) void k_nf4_quantize(const uint16_t* __restrict__ W, int64_t numel,
-                                                           int64_t ncode_blk, uint8_t* __restrict__ codes,
-                                                           float* __restrict__ absmax,
-                                                           unsigned long long* __restrict__ hist, ThrLut lut) {
+__global__ __launch_bounds__(kQuantThreads) void k_nf4_quantize(const uint16_t* __restrict__ W, int64_t numel,
+                                                                int64_t ncode_blk, uint8_t* __restrict__ codes,
+                                                                float* __restrict__ absmax,
+                                                                unsigned long long* __restrict__ sums, ThrLut lut) {
   __shared__ unsigned long long lhist[256];
+  __shared__ unsigned long long limb[kSumLimbs];
   __shared__ float2 slut[kLutBins];
-  const bool dq = hist != nullptr;
-  if (dq) lhist[threadIdx.x] = 0ull;
+  const bool dq = sums != nullptr;
+  if (dq && threadIdx.x < 256) lhist[threadIdx.x] = 0ull;
+  if (dq && threadIdx.x < kSumLimbs) limb[threadIdx.x] = 0ull;
   if (threadIdx.x < kLutBins) slut[threadIdx.x] = make_float2(lut.t[threadIdx.x], __uint_as_float(lut.base[threadIdx.x]));
   __syncthreads();
   const int sub = threadIdx.x & (L - 1);
   const int64_t nblk = (numel + 8 * L - 1) / (8 * L);
-  const int64_t stride = (int64_t)gridDim.x * (kThreads / L);
-  for (int64_t blk = (int64_t)blockIdx.x * (kThreads / L) + (threadIdx.x / L); blk < ncode_blk; blk += stride) {
+  const int64_t stride = (int64_t)gridDim.x * (kQuantThreads / L);
+  for (int64_t blk = (int64_t)blockIdx.x * (kQuantThreads / L) + (threadIdx.x / L); blk < ncode_blk; blk += stride) {
     const int64_t e0 = blk * (8 * L) + sub * 8;
     uint32_t h[8];
     if (e0 + 8 <= numel) {
@@ -79,58 +85,64 @@ __global__ __launch_bounds__(kThreads) void k_nf4_quantize(const uint16_t* __res
     }
   }
   if (dq) {
-    // one of kHistCopies global copies per workgroup, so the few busy bins do not
-    // serialize every workgroup's atomics on one address
     __syncthreads();
-    const unsigned long long v = lhist[threadIdx.x];
-    if (v) atomicAdd(&hist[(blockIdx.x % kHistCopies) * 256 + threadIdx.x], v);
+    // bin E adds hist[E] << E: its low 64 bits over limbs E / 32 and E / 32 + 1, the bits shifted
+    // out into limb E / 32 + 2 (E <= 254 keeps that below kSumLimbs); each limb collects at most
+    // 96 terms below 2^32.  Exponent 255 (infinite or NaN weights) is left out.
+    if (threadIdx.x < 255) {
+      const unsigned long long v = lhist[threadIdx.x];
+      if (v) {
+        const int l0 = threadIdx.x >> 5, sh = threadIdx.x & 31;
+        const unsigned long long lo = v << sh, hi = sh ? v >> (64 - sh) : 0ull;
+        atomicAdd(&limb[l0], lo & 0xFFFFFFFFull);
+        atomicAdd(&limb[l0 + 1], lo >> 32);
+        if (hi) atomicAdd(&limb[l0 + 2], hi);
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x < kSumLimbs) sums[(int64_t)blockIdx.x * kSumLimbs + threadIdx.x] = limb[threadIdx.x];
   }
 }
 
-// mu = fl32(S / nblk), S = the exact sum of all block constants rounded once to float64.
-// hist[E] = sum of the 8-bit significands (implicit bit included) of the constants whose
-// bf16 exponent field is E, so S = sum_E hist[E] * 2^(E - 134).  The exact integer
-// sum_E hist[E] << E is built in 64-bit words, then rounded to nearest even.  Called by all
-// kThreads threads of a workgroup; every thread gets mu.
-__device__ float exact_mean(const unsigned long long* __restrict__ hist, int64_t nblk) {
-  __shared__ unsigned long long tot[256];
-  __shared__ unsigned long long nonzero[4];
+// mu = fl32(S / nblk), S = the exact sum of all block constants rounded once to float64.  A
+// constant with bf16 exponent field E and significand m (implicit bit included) is
+// m * 2^(E - 134), so S * 2^134 is an integer: the sum of the quantize workgroups' slots, added
+// word by word (word k weighs 2^(32 k)) and carried once, then rounded to nearest even.  Called by all kThreads threads of a workgroup; every thread gets mu.
+__device__ float exact_mean(const unsigned long long* __restrict__ sums, int nslots, int64_t nblk) {
+  constexpr int G = kThreads / kSumLimbs;   // 25 threads per limb
+  __shared__ unsigned long long tot[kSumLimbs];
   __shared__ float mu_s;
-  {
-    unsigned long long v = 0;
-#pragma unroll 16
-    for (int c = 0; c < kHistCopies; ++c) v += hist[c * 256 + threadIdx.x];
-    tot[threadIdx.x] = v;
-    const unsigned long long b = __ballot(v != 0ull);
-    if ((threadIdx.x & 63) == 0) nonzero[threadIdx.x >> 6] = b;
+  if (threadIdx.x < kSumLimbs) tot[threadIdx.x] = 0ull;
+  __syncthreads();
+  if (threadIdx.x < G * kSumLimbs) {
+    // thread t adds limb t % kSumLimbs of slots t / kSumLimbs, + G, + 2 G, ... (at most
+    // kQuantSlots slots);
+    // threads read consecutive words; every load is issued before the first add
+    constexpr int PER = (kQuantSlots + G - 1) / G;
+    const int k = threadIdx.x % kSumLimbs, g = threadIdx.x / kSumLimbs;
+    unsigned long long v[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int sl = g + u * G;
+      v[u] = sl < nslots ? sums[sl * kSumLimbs + k] : 0ull;
+    }
+    unsigned long long a = 0ull;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) a += v[u];
+    atomicAdd(&tot[k], a);
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    constexpr int NW = 7;   // 448 bits: 2^254 * 2^64 fits
+    // limb sums are below 2^49 (at most kQuantSlots slots of words below 2^39): one carry pass
+    // gives 32-bit limbs
+    constexpr int NW = kSumLimbs / 2;   // 64-bit words
     unsigned long long acc[NW];
-#pragma unroll
-    for (int k = 0; k < NW; ++k) acc[k] = 0ull;
-    // only the occupied exponent bins, in increasing order (bin 0 only ever holds zeros)
-    for (int wv = 0; wv < 4; ++wv)
-    for (unsigned long long bits = nonzero[wv]; bits; bits &= bits - 1ull) {
-      const int E = wv * 64 + __builtin_ctzll(bits);
-      if (E == 0 || E == 255) continue;
-      const unsigned long long v = tot[E];
-      const int w = E >> 6, sh = E & 63;
-      const unsigned long long lo = v << sh;
-      const unsigned long long hi = sh ? (v >> (64 - sh)) : 0ull;
-      unsigned long long s = acc[w] + lo;
-      unsigned long long carry = s < lo;
-      acc[w] = s;
-      s = acc[w + 1] + hi;
-      unsigned long long c2 = s < hi;
-      s += carry;
-      c2 += (s < carry);
-      acc[w + 1] = s;
-      for (int k = w + 2; c2 && k < NW; ++k) {
-        acc[k] += 1ull;
-        c2 = (acc[k] == 0ull);
-      }
+    unsigned long long carry = 0;
+    for (int k = 0; k < kSumLimbs; ++k) {
+      const unsigned long long t = tot[k] + carry;
+      const unsigned long long l = t & 0xFFFFFFFFull;
+      if (k & 1) acc[k >> 1] |= l << 32; else acc[k >> 1] = l;
+      carry = t >> 32;
     }
     int top = -1;
     for (int k = NW - 1; k >= 0; --k)
@@ -162,28 +174,51 @@ __device__ float exact_mean(const unsigned long long* __restrict__ hist, int64_t
 }
 
 // Groups of 256 block constants, one wave per group (4 constants per lane, a wave-wide
-// max), grid-stride over the groups.  Each workgroup first forms mu from the histogram itself
+// max), grid-stride over the groups.  Each workgroup first forms mu from the slots itself
 // (the same exact sum in every workgroup, so no launch of its own); the first one stores it.
 // Then c1 = max |absmax - mu| / 448 and the E4M3 codes of the group.
 __global__ __launch_bounds__(kThreads) void k_dq_encode(const float* __restrict__ absmax, int64_t nblk,
-                                                        const unsigned long long* __restrict__ hist,
+                                                        const unsigned long long* __restrict__ sums, int nslots,
                                                         float* __restrict__ mu_out, uint8_t* __restrict__ c2,
                                                         float* __restrict__ c1_out) {
   static_assert(kSuper == 4 * 64, "a group is one wave of 4 constants per lane");
-  const float mu = exact_mean(hist, nblk);
-  if (blockIdx.x == 0 && threadIdx.x == 0) *mu_out = mu;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t nsup = (nblk + kSuper - 1) / kSuper;
-  for (int64_t j = (int64_t)blockIdx.x * (kThreads / 64) + wave; j < nsup; j += (int64_t)gridDim.x * (kThreads / 64)) {
+  const int64_t j0 = (int64_t)blockIdx.x * (kThreads / 64) + wave;
+  // the constants of a group; entries past the end are marked and become mu (so x - mu = 0)
+  auto load = [&](int64_t j, float (&x)[4], bool (&in)[4]) {
     const int64_t b0 = j * kSuper + lane * 4;
-    float x[4];
     if (b0 + 4 <= nblk) {
       const float4 a = *reinterpret_cast<const float4*>(absmax + b0);
       x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) in[i] = true;
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) x[i] = b0 + i < nblk ? absmax[b0 + i] : mu;   // past the end: x = 0
+      for (int i = 0; i < 4; ++i) {
+        in[i] = b0 + i < nblk;
+        x[i] = in[i] ? absmax[b0 + i] : 0.0f;
+      }
     }
+  };
+  // the first group's loads are in flight while mu is formed
+  float x0[4] = {0.f, 0.f, 0.f, 0.f};
+  bool in0[4] = {false, false, false, false};
+  if (j0 < nsup) load(j0, x0, in0);
+  const float mu = exact_mean(sums, nslots, nblk);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *mu_out = mu;
+  for (int64_t j = j0; j < nsup; j += (int64_t)gridDim.x * (kThreads / 64)) {
+    const int64_t b0 = j * kSuper + lane * 4;
+    float x[4];
+    bool in[4];
+    if (j == j0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { x[i] = x0[i]; in[i] = in0[i]; }
+    } else {
+      load(j, x, in);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) if (!in[i]) x[i] = mu;   // past the end: x - mu = 0
     uint32_t m = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -269,34 +304,40 @@ hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_quantize(const uint16_t* W, int64_t numel, int codebook, int block, uint8_t* codes,
-                           float* absmax_f32, unsigned long long* hist, hipStream_t s) {
+int quantize_grid(int64_t numel, int block) {
   const int64_t unit = block > 64 ? block : 64;   // the code buffer holds whole blocks and 64-chunks
   const int64_t ncode_blk = (numel + unit - 1) / unit * (unit / block);
-  const unsigned grid = grid_for(ncode_blk, kThreads / (block / 8), 2048);
+  return (int)grid_for(ncode_blk, kQuantThreads / (block / 8), kQuantSlots);
+}
+
+hipError_t launch_quantize(const uint16_t* W, int64_t numel, int codebook, int block, uint8_t* codes,
+                           float* absmax_f32, unsigned long long* sums, hipStream_t s) {
+  const int64_t unit = block > 64 ? block : 64;
+  const int64_t ncode_blk = (numel + unit - 1) / unit * (unit / block);
+  const unsigned grid = (unsigned)quantize_grid(numel, block);
   const ThrLut& tab = thr_lut_host(codebook);
   ProfScope ps("k_nf4_quantize", s);
   if (block == 32)
-    hipLaunchKernelGGL(k_nf4_quantize<4>, dim3(grid), dim3(kThreads), 0, s, W, numel, ncode_blk, codes, absmax_f32,
-                       hist, tab);
+    hipLaunchKernelGGL(k_nf4_quantize<4>, dim3(grid), dim3(kQuantThreads), 0, s, W, numel, ncode_blk, codes,
+                       absmax_f32, sums, tab);
   else if (block == 64)
-    hipLaunchKernelGGL(k_nf4_quantize<8>, dim3(grid), dim3(kThreads), 0, s, W, numel, ncode_blk, codes, absmax_f32,
-                       hist, tab);
+    hipLaunchKernelGGL(k_nf4_quantize<8>, dim3(grid), dim3(kQuantThreads), 0, s, W, numel, ncode_blk, codes,
+                       absmax_f32, sums, tab);
   else if (block == 128)
-    hipLaunchKernelGGL(k_nf4_quantize<16>, dim3(grid), dim3(kThreads), 0, s, W, numel, ncode_blk, codes, absmax_f32,
-                       hist, tab);
+    hipLaunchKernelGGL(k_nf4_quantize<16>, dim3(grid), dim3(kQuantThreads), 0, s, W, numel, ncode_blk, codes,
+                       absmax_f32, sums, tab);
   else
-    hipLaunchKernelGGL(k_nf4_quantize<32>, dim3(grid), dim3(kThreads), 0, s, W, numel, ncode_blk, codes, absmax_f32,
-                       hist, tab);
+    hipLaunchKernelGGL(k_nf4_quantize<32>, dim3(grid), dim3(kQuantThreads), 0, s, W, numel, ncode_blk, codes,
+                       absmax_f32, sums, tab);
   return hipGetLastError();
 }
 
-hipError_t launch_dq_encode(const float* absmax_f32, int64_t nblk, const unsigned long long* hist, float* mu,
+hipError_t launch_dq_encode(const float* absmax_f32, int64_t nblk, const unsigned long long* sums, int nslots, float* mu,
                             uint8_t* c2, float* c1, hipStream_t s) {
   const int64_t nsup = (nblk + kSuper - 1) / kSuper;
   ProfScope ps("k_dq_encode", s);
-  hipLaunchKernelGGL(k_dq_encode, dim3(grid_for(nsup, kThreads / 64, 1024)), dim3(kThreads), 0, s, absmax_f32, nblk, hist, mu, c2,
-                     c1);
+  hipLaunchKernelGGL(k_dq_encode, dim3(grid_for(nsup, kThreads / 64, 1024)), dim3(kThreads), 0, s, absmax_f32, nblk,
+                     sums, nslots, mu, c2, c1);
   return hipGetLastError();
 }
 
