@@ -479,6 +479,14 @@ qlora_status qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, const uint1
       float* const dxpart = L.partial + lora_partial_floats(pg);
       const GFold gf{fold_g ? L.partial : nullptr, pg.splits, pg.tiles_j, scale, L.Gs};
       QL_HIP(launch_dx_gemm_split(dY, M, in, out, v, (int)dst, dxpart, stream));
+      if (M <= 16) {
+        // one token group: the epilogue also forms dA (from its Gs) and dB (extra workgroups),
+        // so the backward ends here
+        const GradFold gr{X, T, dY, dA, dB, out, scale};
+        QL_HIP(launch_dx_split_epilogue(dxpart, (int)dx_split_count(out, dst), M, in, L.Gs, rp, A, r, dX, gf, stream,
+                                        &gr));
+        return QLORA_OK;
+      }
       QL_HIP(launch_dx_split_epilogue(dxpart, (int)dx_split_count(out, dst), M, in, L.Gs, rp, A, r, dX, gf, stream));
     } else {
       QL_HIP(launch_dx_gemm(dY, M, in, out, v, L.Gs, rp, A, r, dX, stream));

@@ -206,14 +206,73 @@ __global__ __launch_bounds__(NT) void k_bwd_dx_nf4_gemm(DxParams p) {
 // the tokens t / 64 + 4 q of the group.  Rows i0..i0+63 of A are one contiguous run of
 // 64 r values: loaded coalesced and kept transposed in LDS ([j][64]); the group's rows of
 // Gs are kept as fp32.  All loads are issued before any is used.
+// Sums over the (at most 16) tokens of one group for the adapter gradients: thread t keeps the
+// 16 token values of its column of one operand in registers (zero past the group) and reads the
+// other operand's 16 values as four broadcast 16-byte LDS reads from a transposed [row][16]
+// tile; the tokens are added in order.
+__device__ __forceinline__ float dot16(const float* __restrict__ row16, const float (&v)[16]) {
+  float sum = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float4 a = *reinterpret_cast<const float4*>(row16 + 4 * q);
+    sum = __builtin_fmaf(a.x, v[4 * q + 0], sum);
+    sum = __builtin_fmaf(a.y, v[4 * q + 1], sum);
+    sum = __builtin_fmaf(a.z, v[4 * q + 2], sum);
+    sum = __builtin_fmaf(a.w, v[4 * q + 3], sum);
+  }
+  return sum;
+}
+
+// dB[j][o0 + oo] = fl32(s * sum_m T[m][j] dY[m][o0 + oo]) for j < r: T transposed in LDS
+// ([j][16]), each thread one column oo (its 16 dY values in registers) and the rows j of its
+// wave, consecutive threads on consecutive columns.
+__device__ __forceinline__ void grad_dB_block(const GradFold& g, int64_t M, int64_t r, int64_t o0, float* sTt,
+                                              float* sY) {
+  const int t = threadIdx.x;
+  const int Mg = (int)M;
+  // every load is issued before the first LDS store: T (at most 16 x 256 values, 16 per
+  // thread) and the 16 x 64 values of dY (4 per thread)
+  uint16_t tv[16], yv[4];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int e = t + 256 * k, m = e / (int)r;
+    tv[k] = e < 16 * (int)r && m < Mg ? g.T[e] : (uint16_t)0;   // T[m][j] at m r + j = e
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int e = t + 256 * k, m = e >> 6, oo = e & 63;
+    yv[k] = m < Mg && o0 + oo < g.N ? g.dY[m * g.N + o0 + oo] : (uint16_t)0;
+  }
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int e = t + 256 * k, m = e / (int)r, j = e - m * (int)r;
+    if (e < 16 * (int)r) sTt[j * 16 + m] = bf16_to_f32(tv[k]);
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) sY[t + 256 * k] = bf16_to_f32(yv[k]);
+  __syncthreads();
+  const int oo = t & 63;
+  float y[16];
+#pragma unroll
+  for (int m = 0; m < 16; ++m) y[m] = sY[m * 64 + oo];
+  for (int j = t >> 6; j < (int)r; j += 4) {
+    const float sum = dot16(sTt + j * 16, y);
+    if (o0 + oo < g.N) g.dB[j * g.N + o0 + oo] = __fmul_rn(g.scale, sum);
+  }
+}
+
 __global__ __launch_bounds__(256) void k_dx_split_epilogue(const float* __restrict__ partial, int splits, int64_t M,
                                                           int64_t K, const uint16_t* __restrict__ Gs, int64_t rp,
                                                           const uint16_t* __restrict__ A, int64_t r,
-                                                          uint16_t* __restrict__ dX, GFold gf) {
+                                                          uint16_t* __restrict__ dX, GFold gf, GradFold gr) {
   __shared__ __attribute__((aligned(16))) float sG[16 * 256];
   __shared__ __attribute__((aligned(16))) uint16_t sA[256 * 64];
   const int t = threadIdx.x;
   const int c = t & 63, mq = t >> 6;
+  if (gr.dA && (int64_t)blockIdx.x >= K / 64) {   // a dB workgroup (one token group)
+    grad_dB_block(gr, M, r, ((int64_t)blockIdx.x - K / 64) * 64, sG, reinterpret_cast<float*>(sA));
+    return;
+  }
   const int64_t i0 = (int64_t)blockIdx.x * 64;   // K is a multiple of 64: every column exists
   const int64_t m0 = (int64_t)blockIdx.y * 16;
   const int Mg = (int)min<int64_t>(16, M - m0);
@@ -238,6 +297,14 @@ __global__ __launch_bounds__(256) void k_dx_split_epilogue(const float* __restri
   for (int u = 0; u < 8; ++u) {
     const int idx = t + 256 * u;
     av[u] = ld16(rA, idx < apieces ? abase + (uint32_t)idx * 16 : aend);
+  }
+  // dA: this block's 64 columns of X for the (at most 16) tokens, four per thread (8 bytes of
+  // one row; rows past the tokens read zero), loaded now so they arrive with the rest
+  uint2 xv = make_uint2(0u, 0u);
+  if (gr.dA) {
+    const int m = t >> 4, il = (t & 15) * 4;
+    const rsrc_t rX = make_rsrc(gr.X, (uint64_t)M * K * 2);
+    xv = gemm::ld8(rX, m < Mg ? (uint32_t)((m * K + i0 + il) * 2) : (uint32_t)(M * K * 2));
   }
   // Gs rows of the group: Mg rp values, at most 2 pieces per thread (when Gs is in memory)
   const rsrc_t rG = make_rsrc(Gs, (uint64_t)M * rp * 2);
@@ -326,6 +393,30 @@ __global__ __launch_bounds__(256) void k_dx_split_epilogue(const float* __restri
     const int m = mq + 4 * q;
     if (m < Mg) dX[(m0 + m) * K + i0 + c] = (uint16_t)f32_to_bf16_bits(__fadd_rn(acc[q], lora[q]));
   }
+  if (gr.dA) {
+    // dA[i0 + il][j] = sum over the tokens of X[m][i0 + il] Gs[m][j] (Gs in sG; the group holds
+    // every token): X transposed in LDS ([il][16], sA is free again), each thread one column j
+    // (its 16 Gs values in registers) and the rows il of its wave, consecutive threads on
+    // consecutive j
+    float* const sXt = reinterpret_cast<float*>(sA);
+    __syncthreads();
+    {
+      const int m = t >> 4, il = (t & 15) * 4;
+      sXt[(il + 0) * 16 + m] = bf16_to_f32(xv.x & 0xFFFFu);
+      sXt[(il + 1) * 16 + m] = bf16_to_f32(xv.x >> 16);
+      sXt[(il + 2) * 16 + m] = bf16_to_f32(xv.y & 0xFFFFu);
+      sXt[(il + 3) * 16 + m] = bf16_to_f32(xv.y >> 16);
+    }
+    __syncthreads();
+    for (int jb = 0; jb < (int)r; jb += 64) {
+      const int j = jb + (t & 63);
+      float g[16];
+#pragma unroll
+      for (int m = 0; m < 16; ++m) g[m] = m < Mg && j < (int)r ? sG[m * 256 + j] : 0.0f;
+      if (j < (int)r)
+        for (int il = t >> 6; il < 64; il += 4) gr.dA[(i0 + il) * r + j] = dot16(sXt + il * 16, g);
+    }
+  }
 }
 
 // dispatch over the template flags (DQ, RAGGED, BM, SPLIT)
@@ -381,10 +472,13 @@ hipError_t launch_dx_gemm_split(const uint16_t* dY, int64_t M, int64_t K, int64_
 
 hipError_t launch_dx_split_epilogue(const float* partial, int splits, int64_t M, int64_t K, const uint16_t* Gs,
                                     int64_t rp, const uint16_t* A, int64_t r, uint16_t* dX, const GFold& gf,
-                                    hipStream_t s) {
+                                    hipStream_t s, const GradFold* grads) {
+  if (grads && M > 16) return hipErrorInvalidValue;   // the gradients need every token in one group
+  const GradFold gr = grads ? *grads : GradFold{nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0.0f};
+  const int64_t nb = K / 64 + (grads ? (grads->N + 63) / 64 : 0);
   ProfScope ps("k_dx_split_epilogue", s);
-  const dim3 grid((unsigned)(K / 64), (unsigned)((M + 15) / 16)), block(256);
-  hipLaunchKernelGGL(k_dx_split_epilogue, grid, block, 0, s, partial, splits, M, K, Gs, rp, A, r, dX, gf);
+  const dim3 grid((unsigned)nb, (unsigned)((M + 15) / 16)), block(256);
+  hipLaunchKernelGGL(k_dx_split_epilogue, grid, block, 0, s, partial, splits, M, K, Gs, rp, A, r, dX, gf, gr);
   return hipGetLastError();
 }
 

@@ -140,9 +140,21 @@ struct GFold {
   float scale;
   uint16_t* Gs_out;
 };
+// With at most 16 tokens (one token group) the same launch can also finish the adapter
+// gradients (dA == NULL: it does not): each dX workgroup forms dA = X^T Gs for its 64 rows of
+// dA, and ceil(N / 64) more workgroups form dB = s T^T dY for 64 columns of dB each.
+struct GradFold {
+  const uint16_t* X;    // [M][K]
+  const uint16_t* T;    // [M][r], bf16(X A)
+  const uint16_t* dY;   // [M][N]
+  float* dA;            // [K][r]
+  float* dB;            // [r][N]
+  int64_t N;
+  float scale;
+};
 hipError_t launch_dx_split_epilogue(const float* partial, int splits, int64_t M, int64_t K, const uint16_t* Gs,
                                     int64_t rp, const uint16_t* A, int64_t r, uint16_t* dX, const GFold& gf,
-                                    hipStream_t s);
+                                    hipStream_t s, const GradFold* grads = nullptr);
 
 // ---- adapter merge (merge.hip): out [N][K] = bf16(deq(W) + scale (A B)^T), K % 64 == 0 -------
 hipError_t launch_merge_adapter(const NF4View& w, int64_t N, int64_t K, const uint16_t* A, const uint16_t* B, int64_t r,

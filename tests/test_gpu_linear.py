@@ -171,6 +171,21 @@ def test_split_backward(M, din, dout, r):
     _check_full(inp, save_T=False, label=f"splitdx{(M, din, dout, r)} recompute T")
 
 
+GRADS_IN_EPILOGUE = [
+    # (M, in, out, r): at most 16 tokens on the split dX path: its epilogue also forms dA
+    # (per 64-row block) and dB (extra workgroups, ragged last block when out % 64 != 0)
+    (5, 2048, 1000, 256),      # largest rank, 40 columns in the last dB block
+    (16, 4096, 4096, 64),      # the 4096-square layer at 16 tokens
+]
+
+
+@pytest.mark.parametrize("M,din,dout,r", GRADS_IN_EPILOGUE)
+def test_adapter_grads_in_split_epilogue(M, din, dout, r):
+    inp = workloads.custom_linear(M, din, dout, r, seed=5 * M + din + dout + r)
+    _check_full(inp, label=f"grads-epi{(M, din, dout, r)}")
+    _check_full(inp, save_T=False, label=f"grads-epi{(M, din, dout, r)} recompute-T")
+
+
 @pytest.mark.parametrize("dq,block", [(False, 64), (True, 128), (True, 32)])
 def test_split_backward_formats(dq, block):
     inp = workloads.custom_linear(48, 512, 1000, 16, seed=49 + block)
