@@ -465,12 +465,13 @@ qlora_status qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, const uint1
   LoraProblem pg = lora_problem(gemm_G(dY, B, M, out, r), LoraEpi{nullptr, 0, 0.0f, L.Gs, rp, scale, nullptr, 0.0f},
                                 kMaxSplits);
   pg.partial = L.partial;
-  QL_HIP(launch_lora(pg, nullptr, "k_lora_dyb", stream));
   const int64_t dst = dX ? dx_split_stages(M, in, out) : 0;
   // with the split dX and at most 64 tokens, its epilogue sums G's partials itself (and stores
   // Gs for dA); with more tokens every one of its in/64 column blocks would repeat that sum for
-  // its token group, which costs more than the reduce launch (measured at 256 and 512 tokens)
+  // its token group, which costs more than the reduce launch (measured at 256 and 512 tokens).
+  // G's split-K workgroups then run inside the split dX launch (nothing there depends on G).
   const bool fold_g = dst && pg.splits > 1 && M <= 64;
+  if (!fold_g) QL_HIP(launch_lora(pg, nullptr, "k_lora_dyb", stream));
   if (pg.splits > 1 && !fold_g) QL_HIP(launch_lora_reduce(pg, nullptr, "k_lora_dyb_reduce", stream));
   if (dX) {
     if (dst) {
@@ -478,7 +479,7 @@ qlora_status qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, const uint1
       // then the slices' sum plus Gs A^T in one epilogue
       float* const dxpart = L.partial + lora_partial_floats(pg);
       const GFold gf{fold_g ? L.partial : nullptr, pg.splits, pg.tiles_j, scale, L.Gs};
-      QL_HIP(launch_dx_gemm_split(dY, M, in, out, v, (int)dst, dxpart, stream));
+      QL_HIP(launch_dx_gemm_split(dY, M, in, out, v, (int)dst, dxpart, stream, fold_g ? &pg : nullptr));
       if (M <= 16) {
         // one token group: the epilogue also forms dA (from its Gs) and dB (extra workgroups),
         // so the backward ends here

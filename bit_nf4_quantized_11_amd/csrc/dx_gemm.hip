@@ -17,6 +17,7 @@
 #include "common.h"
 #include "gemm_core.h"
 #include "kernels.h"
+#include "lora_tile.h"
 
 namespace qlora {
 
@@ -38,6 +39,9 @@ struct DxParams {
   // split mode: slices of `spl` stages, fp32 partials [split][M][K], no adapter stages
   float* partial;
   uint32_t spl;
+  // split mode: the first nlora workgroups compute the split-K partials of G = dY B^T instead
+  LoraProblem lg;
+  int nlora;
 };
 
 struct WRegs {
@@ -60,10 +64,20 @@ __global__ __launch_bounds__(NT) void k_bwd_dx_nf4_gemm(DxParams p) {
   uint16_t* const sT[2] = {smem, smem + TILE_T};
   uint16_t* const sF[2] = {smem + 2 * TILE_T, smem + 2 * TILE_T + TILE_F};
 
+  int64_t bid = blockIdx.x;
+  if constexpr (SPLIT) {
+    // the first nlora workgroups compute G's partials (independent of the dX slices: the
+    // epilogue adds both; measured, placing them after the dX workgroups is slower)
+    if (bid < p.nlora) {
+      lora_tile::tile_kc512(p.lg, bid, smem);
+      return;
+    }
+    bid -= p.nlora;
+  }
   const int64_t tiles_t = (p.M + BT - 1) / BT, tiles_f = (p.K + BF - 1) / BF;
-  const uint32_t split = SPLIT ? (uint32_t)(blockIdx.x / (tiles_t * tiles_f)) : 0u;
+  const uint32_t split = SPLIT ? (uint32_t)(bid / (tiles_t * tiles_f)) : 0u;
   int64_t tt, tf;
-  tile_of(tiles_t, tiles_f, tt, tf, SPLIT ? (int64_t)blockIdx.x - (int64_t)split * tiles_t * tiles_f : -1);
+  tile_of(tiles_t, tiles_f, tt, tf, SPLIT ? bid - (int64_t)split * tiles_t * tiles_f : -1);
   const uint32_t m0 = (uint32_t)(tt * BT), k0 = (uint32_t)(tf * BF);
   const uint32_t nkb = (uint32_t)(p.K / 64);
   const uint32_t N = (uint32_t)p.N;
@@ -443,7 +457,7 @@ hipError_t launch_dx_gemm(const uint16_t* dY, int64_t M, int64_t K, int64_t N, c
   // 64-element code chunks, and blocks (one constant each; in is a multiple of the block size)
   const uint64_t nchunk = (uint64_t)N * K / 64, nblk = ((uint64_t)N * K) >> w.bshift;
   DxParams p{dY, M, K, N, w, nchunk * kBlockBytes, w.dq ? nblk : nblk * 4, w.dq ? ((nblk + 255) / 256) * 4 : 0,
-             Gs, rp, A, r, dX, nf4_table(w.cb), nullptr, 0};
+             Gs, rp, A, r, dX, nf4_table(w.cb), nullptr, 0, LoraProblem{}, 0};
   const int64_t tiles = ((M + BT - 1) / BT) * ((K + BF - 1) / BF);
   ProfScope ps("k_bwd_dx_nf4_gemm", s);
   const dim3 grid((unsigned)tiles), block(NT);
@@ -454,16 +468,23 @@ hipError_t launch_dx_gemm(const uint16_t* dY, int64_t M, int64_t K, int64_t N, c
 }
 
 hipError_t launch_dx_gemm_split(const uint16_t* dY, int64_t M, int64_t K, int64_t N, const NF4View& w, int stages,
-                                float* partial, hipStream_t s) {
+                                float* partial, hipStream_t s, const LoraProblem* g_partials) {
   const uint64_t nchunk = (uint64_t)N * K / 64, nblk = ((uint64_t)N * K) >> w.bshift;
   const uint32_t spl = (uint32_t)stages;
   DxParams p{dY, M, K, N, w, nchunk * kBlockBytes, w.dq ? nblk : nblk * 4, w.dq ? ((nblk + 255) / 256) * 4 : 0,
-             nullptr, 0, nullptr, 0, nullptr, nf4_table(w.cb), partial, spl};
+             nullptr, 0, nullptr, 0, nullptr, nf4_table(w.cb), partial, spl, LoraProblem{}, 0};
+  if (g_partials) {
+    // both operands contiguous along the reduction, split-K partials only
+    if (g_partials->g.a_sk != 1 || g_partials->g.b_sk != 1 || g_partials->splits < 2 || !g_partials->partial)
+      return hipErrorInvalidValue;
+    p.lg = *g_partials;
+    p.nlora = (int)(g_partials->tiles_i * g_partials->tiles_j * g_partials->splits);
+  }
   const int64_t tiles = ((M + BT - 1) / BT) * ((K + BF - 1) / BF);
   const int64_t nred = (N + 63) / 64;
   const int64_t used = (nred + spl - 1) / spl;   // slices, each with at least one stage
   ProfScope ps("k_bwd_dx_nf4_gemm", s);
-  const dim3 grid((unsigned)(tiles * used)), block(NT);
+  const dim3 grid((unsigned)(p.nlora + tiles * used)), block(NT);
   const bool ragged = (N % 64) != 0;
   const int bm = w.bshift == 6 ? 0 : w.bshift > 6 ? 1 : 2;
   launch_dx_variant<0, true>(w.dq != 0, ragged, bm, grid, block, p, s);

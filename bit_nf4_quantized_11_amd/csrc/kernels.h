@@ -129,8 +129,11 @@ hipError_t launch_dx_gemm(const uint16_t* dY, int64_t M, int64_t K, int64_t N, c
                           hipStream_t s);
 // few tokens: the reduction in slices of `stages` stages, fp32 partials [slice][M][K]
 // (no adapter term), then the epilogue sums the slices in order, adds Gs A^T, rounds once
+// g_partials (optional): a split-K product (both operands contiguous along the reduction, at
+// least 2 splits, its partial buffer set) whose workgroups run first in the same launch: G's
+// partials for the epilogue's fold, without a launch of their own.
 hipError_t launch_dx_gemm_split(const uint16_t* dY, int64_t M, int64_t K, int64_t N, const NF4View& w, int stages,
-                                float* partial, hipStream_t s);
+                                float* partial, hipStream_t s, const LoraProblem* g_partials = nullptr);
 // G still in split-K partials of the rank-r kernel (partial == NULL: Gs is in memory already):
 // the epilogue forms Gs = bf16(scale G) itself and stores it to Gs_out [M][rp] for dA.
 struct GFold {
