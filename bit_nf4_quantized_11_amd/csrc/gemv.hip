@@ -48,7 +48,7 @@ constexpr int GROWS = 64;         // adapter columns per adapter workgroup
 constexpr int ACH = 64;           // rows of A per LDS chunk (8 KiB)
 constexpr int XAS = 72;           // X chunk row stride in the adapter workgroups (64 + 8 padding)
 constexpr int KA = 2048;          // rows of A per adapter slice beside the weight pass
-constexpr int kSlotsPerCU = 2;    // resident workgroups per CU the grid is sized for (TG = 1)
+constexpr int kSlotsPerCU = 1;    // resident workgroups per CU the grid is sized for (TG = 1)
 constexpr int RG_ROUND = 4;       // row groups x token groups per round (one LDS hand-over each)
 
 // LDS: weight groups use two buffers of RG_ROUND [8 waves][64 lanes] float4 tiles; adapter
